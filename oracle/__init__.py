@@ -1,0 +1,221 @@
+"""CPU oracle for MSA sparse-layer decode attention -- TEST INFRASTRUCTURE ONLY.
+
+A ctypes wrapper around ``msa_oracle.c`` (plain C, double precision).  Only the
+tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package; the library under ``block_sparse_paged_amd`` never does.
+
+Every function takes CPU torch tensors holding the exact bytes the GPU sees
+(uint8 E4M3FN codes, bf16, float32, int32) and returns float64 numpy arrays.
+``build()`` compiles the shared object with gcc.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "msa_oracle.c")
+_LIB = os.environ.get("MSA_ORACLE_LIB") or os.path.join(_HERE, "libmsa_oracle.so")
+
+F32, BF16, E4M3FN = 0, 1, 2
+_ERRORS = {1: "bad argument", 2: "physical page out of range", 3: "seq_len out of range",
+           4: "duplicate block id in a selection", 5: "NaN in a visible position"}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math: IEEE double throughout)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-o", tmp, _SRC, "-lm"],
+                       check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB):
+                build(force=True)
+            lib = ctypes.CDLL(_LIB)
+            i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+            lib.orc_e4m3fn_value.restype = dbl
+            lib.orc_e4m3fn_value.argtypes = [ctypes.c_uint8]
+            lib.orc_bf16_value.restype = dbl
+            lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+            lib.orc_block_score.restype = ctypes.c_int
+            lib.orc_block_score.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, vp, vp,
+                                            i64, i64, i64, i64, i64, i64, dbl, i64, i64, vp]
+            lib.orc_select_topk.restype = ctypes.c_int
+            lib.orc_select_topk.argtypes = [vp, i64, i64, i64, vp]
+            lib.orc_sparse_decode.restype = ctypes.c_int
+            lib.orc_sparse_decode.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, vp,
+                                              i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                              dbl, dbl, dbl, i64, i64, vp]
+            lib.orc_dense_attention.restype = ctypes.c_int
+            lib.orc_dense_attention.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp,
+                                                i64, i64, i64, i64, i64, i64, i64, i64,
+                                                dbl, dbl, dbl, i64, i64, vp]
+            _lib = lib
+    return _lib
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise OracleError(f"oracle precondition failed: {_ERRORS.get(rc, rc)}")
+
+
+def _raw(t: torch.Tensor) -> tuple[np.ndarray, int]:
+    """Contiguous host bytes of a tensor and its oracle dtype code."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return t.view(torch.uint8).numpy(), E4M3FN
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy(), BF16
+    if t.dtype == torch.float32:
+        return t.numpy(), F32
+    if t.dtype == torch.int32:
+        return t.numpy(), -1
+    raise TypeError(f"oracle: unsupported dtype {t.dtype}")
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _ranges(n0: int, n1: int, threads: int):
+    threads = max(1, min(threads, n1 - n0))
+    step = (n1 - n0 + threads - 1) // threads
+    return [(a, min(a + step, n1)) for a in range(n0, n1, step)]
+
+
+def e4m3fn_value(code: int) -> float:
+    return _load().orc_e4m3fn_value(code)
+
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16_value(bits & 0xFFFF)
+
+
+def block_score(q_idx, index_k, block_table, seq_lens, T: int, idx_scale: float,
+                n_range: Optional[tuple[int, int]] = None, threads: int = 1) -> np.ndarray:
+    """scores [N, MB] float64; rows outside ``n_range`` are NaN."""
+    lib = _load()
+    q, qd = _raw(q_idx)
+    k, kd = _raw(index_k)
+    bt, _ = _raw(block_table)
+    sl, _ = _raw(seq_lens)
+    R, MB = bt.shape
+    P, B, Di = k.shape
+    N = R * T
+    n0, n1 = n_range if n_range is not None else (0, N)
+    out = np.full((N, MB), np.nan, dtype=np.float64)
+
+    def run(a, b):
+        return lib.orc_block_score(_ptr(q), qd, _ptr(k), kd, _ptr(bt), _ptr(sl), R, T, MB, P, B,
+                                   Di, float(idx_scale), a, b, _ptr(out))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        for rc in ex.map(lambda ab: run(*ab), _ranges(n0, n1, threads)):
+            _check(rc)
+    return out
+
+
+def select_topk(scores, k: int) -> np.ndarray:
+    """topk_idx [N, k] int32 from a score sheet (float64 or float32 values)."""
+    lib = _load()
+    s = np.ascontiguousarray(np.asarray(scores, dtype=np.float64))
+    N, MB = s.shape
+    out = np.empty((N, k), dtype=np.int32)
+    _check(lib.orc_select_topk(_ptr(s), N, MB, k, _ptr(out)))
+    return out
+
+
+def sparse_decode(q, k_cache, v_cache, block_table, seq_lens, topk_idx, T: int,
+                  sm_scale: float, k_scale: float, v_scale: float,
+                  n_range: Optional[tuple[int, int]] = None, threads: int = 1) -> np.ndarray:
+    """out [N, Hq, D] float64 (rows outside ``n_range`` are NaN)."""
+    lib = _load()
+    qa, qd = _raw(q)
+    ka, kvd = _raw(k_cache)
+    va, _ = _raw(v_cache)
+    bt, _ = _raw(block_table)
+    sl, _ = _raw(seq_lens)
+    tk, _ = _raw(torch.as_tensor(topk_idx, dtype=torch.int32))
+    R, MB = bt.shape
+    P, B, Hkv, D = ka.shape
+    N, Hq, _ = qa.shape
+    K = tk.shape[1]
+    n0, n1 = n_range if n_range is not None else (0, N)
+    out = np.full((N, Hq, D), np.nan, dtype=np.float64)
+
+    def run(a, b):
+        return lib.orc_sparse_decode(_ptr(qa), qd, _ptr(ka), _ptr(va), kvd, _ptr(bt), _ptr(sl),
+                                     _ptr(tk), R, T, MB, P, B, Hq, Hkv, D, K, float(sm_scale),
+                                     float(k_scale), float(v_scale), a, b, _ptr(out))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        for rc in ex.map(lambda ab: run(*ab), _ranges(n0, n1, threads)):
+            _check(rc)
+    return out
+
+
+def dense_attention(q, k_cache, v_cache, block_table, seq_lens, T: int, sm_scale: float,
+                    k_scale: float, v_scale: float,
+                    n_range: Optional[tuple[int, int]] = None, threads: int = 1) -> np.ndarray:
+    lib = _load()
+    qa, qd = _raw(q)
+    ka, kvd = _raw(k_cache)
+    va, _ = _raw(v_cache)
+    bt, _ = _raw(block_table)
+    sl, _ = _raw(seq_lens)
+    R, MB = bt.shape
+    P, B, Hkv, D = ka.shape
+    N, Hq, _ = qa.shape
+    n0, n1 = n_range if n_range is not None else (0, N)
+    out = np.full((N, Hq, D), np.nan, dtype=np.float64)
+
+    def run(a, b):
+        return lib.orc_dense_attention(_ptr(qa), qd, _ptr(ka), _ptr(va), kvd, _ptr(bt), _ptr(sl),
+                                       R, T, MB, P, B, Hq, Hkv, D, float(sm_scale),
+                                       float(k_scale), float(v_scale), a, b, _ptr(out))
+
+    with ThreadPoolExecutor(max_workers=max(1, threads)) as ex:
+        for rc in ex.map(lambda ab: run(*ab), _ranges(n0, n1, threads)):
+            _check(rc)
+    return out
+
+
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (nearest-even) and return them as float64.
+
+    Goes through float32 first only when that step is exact for the comparison
+    at hand; to avoid double rounding it rounds from float64 directly here.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.empty_like(x)
+    flat = x.reshape(-1)
+    res = out.reshape(-1)
+    m, e = np.frexp(flat)                     # flat = m * 2^e, 0.5 <= |m| < 1
+    # bf16 keeps 8 significant bits: round m * 2^8 to nearest even integer
+    scaled = m * 256.0
+    rounded = np.round(scaled)                # numpy rounds half to even
+    res[:] = np.ldexp(rounded / 256.0, e)
+    # subnormal / huge values are not produced by these workloads
+    res[~np.isfinite(flat)] = flat[~np.isfinite(flat)]
+    return out

@@ -1,0 +1,254 @@
+"""Seeded synthetic inputs for MSA sparse-layer decode attention.
+
+This module only draws values and lays them out in the storage formats the
+pages describe (paged FP8 E4M3FN index and K/V caches with 128-token blocks,
+bf16 queries, int32 block tables and sequence lengths).  It holds none of the
+method's arithmetic: no score, selection or attention is computed here.  Both
+the CPU oracle and the HIP library consume the buffers it returns unchanged.
+
+Workload shapes follow the vLLM design note "MiniMax-M3 decode through the
+ATOM kernel library", section "Supported experiment": FP8 main and index
+caches, block size 128, maximum model length 16384, decode/verification rows of
+1 + 3 speculative tokens, buckets of 1/4/8/16 rows, and a 1024-block pool.
+
+Value recipe: N(0,1) draws (numpy PCG64, one independent stream per tensor,
+seeded by ``[seed, tensor_id]``).  FP8 tensors are quantised with a per-tensor
+scale ``amax / 448`` so that the largest magnitude maps to the E4M3FN maximum,
+rounded to nearest-even and saturated to +-448 (torch's float8_e4m3fn cast
+turns overflow into NaN, so the clamp is explicit).  Pool pages that no row
+maps, tail tokens past a row's length, and block-table entries past a row's
+last block are poisoned so that any read of them shows up as NaN.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+BLOCK = 128
+E4M3_MAX = 448.0
+E4M3_NAN_CODE = 0x7F
+
+_TENSOR_IDS = {
+    "q_idx": 1, "index": 2, "q": 3, "k": 4, "v": 5, "perm": 6, "lens": 7, "topk": 8,
+}
+
+
+def _rng(seed: int, name: str) -> np.random.Generator:
+    return np.random.default_rng([int(seed), _TENSOR_IDS[name]])
+
+
+def quantize_e4m3(x: np.ndarray) -> tuple[torch.Tensor, float]:
+    """Per-tensor E4M3FN quantisation: returns (uint8 codes, fp32 scale)."""
+    amax = float(np.max(np.abs(x))) if x.size else 1.0
+    scale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    y = np.clip(x.astype(np.float32) / np.float32(scale), -E4M3_MAX, E4M3_MAX)
+    codes = torch.from_numpy(np.ascontiguousarray(y)).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8), scale
+
+
+def to_bf16(x: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x.astype(np.float32))).to(torch.bfloat16)
+
+
+@dataclasses.dataclass
+class Case:
+    """One synthetic workload.  Tensors live on the CPU; shapes:
+
+    q_idx [N, Di], index_k [P, B, Di], block_table [R, MB], seq_lens [R],
+    q [N, Hq, D], k_cache / v_cache [P, B, Hkv, D].  FP8 tensors are uint8
+    code tensors (``fp8=True``); otherwise float32.  Queries are bf16 when
+    ``fp8`` else float32.
+    """
+    name: str
+    R: int
+    T: int
+    Hq: int
+    Hkv: int
+    D: int
+    Di: int
+    P: int
+    MB: int
+    k: int
+    B: int
+    fp8: bool
+    seq_lens: torch.Tensor
+    block_table: torch.Tensor
+    q_idx: torch.Tensor
+    index_k: torch.Tensor
+    q: Optional[torch.Tensor]
+    k_cache: Optional[torch.Tensor]
+    v_cache: Optional[torch.Tensor]
+    idx_scale: float
+    k_scale: float
+    v_scale: float
+    sm_scale: float
+
+    @property
+    def N(self) -> int:
+        return self.R * self.T
+
+    def visible(self, n: int) -> int:
+        """Key positions visible to query token n (row-causal, new tokens in cache)."""
+        r, t = divmod(n, self.T)
+        return max(0, int(self.seq_lens[r]) - (self.T - 1 - t))
+
+
+def make_case(name: str, *, R: int, T: int, Hq: int, Hkv: int, D: int, Di: int,
+              seq_lens: Sequence[int], P: int, k: int, MB: Optional[int] = None,
+              fp8: bool = True, seed: int = 0, attention: bool = True,
+              shared_pages: bool = False, nan_q_rows: Sequence[int] = (),
+              B: int = BLOCK) -> Case:
+    """Build a paged workload.
+
+    Each row r owns ceil(seq_lens[r] / B) logical blocks mapped to physical pages
+    through a random block table.  With ``shared_pages=False`` rows take disjoint
+    random page sets; with ``True`` every row draws its pages independently from
+    the whole pool (pages may be shared between rows).  Unused pool pages, tail
+    tokens past seq_len and block-table entries past the last block are poisoned.
+    Rows listed in ``nan_q_rows`` get NaN queries (padded rows of a bucket).
+    """
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    assert lens.shape == (R,)
+    nblk = (lens + B - 1) // B
+    if MB is None:
+        MB = int(max(1, nblk.max()))
+    assert nblk.max() <= MB
+    N = R * T
+    prng = _rng(seed, "perm")
+    used = int(nblk.sum())
+    bt = np.zeros((R, MB), dtype=np.int32)
+    if shared_pages:
+        assert P > 1
+        poison_page = P - 1
+        for r in range(R):
+            bt[r, : nblk[r]] = prng.choice(P - 1, size=nblk[r], replace=False)
+        used_pages = np.unique(bt[nblk[:, None] > np.arange(MB)[None, :]])
+    else:
+        assert used < P, "need at least one spare page to serve as the poisoned page"
+        perm = prng.permutation(P).astype(np.int32)
+        off = 0
+        for r in range(R):
+            bt[r, : nblk[r]] = perm[off: off + nblk[r]]
+            off += nblk[r]
+        used_pages = perm[:used]
+        poison_page = int(perm[used])
+    for r in range(R):
+        bt[r, nblk[r]:] = poison_page
+
+    # which (page, token) slots hold real data
+    slot_valid = np.zeros((P, B), dtype=bool)
+    for r in range(R):
+        for j in range(nblk[r]):
+            ntok = min(B, int(lens[r]) - j * B)
+            slot_valid[bt[r, j], :ntok] = True
+    if shared_pages:
+        slot_valid[used_pages] = True  # shared pages are fully written
+
+    def pool(name_: str, shape_tail: tuple) -> tuple[torch.Tensor, float]:
+        g = _rng(seed, name_)
+        vals = g.standard_normal((len(used_pages), B) + shape_tail, dtype=np.float32)
+        if fp8:
+            codes, scale = quantize_e4m3(vals)
+            out = torch.full((P, B) + shape_tail, E4M3_NAN_CODE, dtype=torch.uint8)
+            out[torch.from_numpy(used_pages.astype(np.int64))] = codes
+            mask = torch.from_numpy(~slot_valid)
+            out[mask] = E4M3_NAN_CODE
+            return out, scale
+        out = torch.full((P, B) + shape_tail, float("nan"), dtype=torch.float32)
+        out[torch.from_numpy(used_pages.astype(np.int64))] = torch.from_numpy(vals)
+        out[torch.from_numpy(~slot_valid)] = float("nan")
+        return out, 1.0
+
+    index_k, idx_scale = pool("index", (Di,))
+    qi = _rng(seed, "q_idx").standard_normal((N, Di), dtype=np.float32)
+    q_idx = to_bf16(qi) if fp8 else torch.from_numpy(qi)
+    q = k_cache = v_cache = None
+    k_scale = v_scale = 1.0
+    if attention:
+        k_cache, k_scale = pool("k", (Hkv, D))
+        v_cache, v_scale = pool("v", (Hkv, D))
+        qq = _rng(seed, "q").standard_normal((N, Hq, D), dtype=np.float32)
+        q = to_bf16(qq) if fp8 else torch.from_numpy(qq)
+    for r in nan_q_rows:
+        q_idx[r * T:(r + 1) * T] = float("nan")
+        if q is not None:
+            q[r * T:(r + 1) * T] = float("nan")
+    sm_scale = float(np.float32(1.0 / math.sqrt(D)))
+    return Case(name=name, R=R, T=T, Hq=Hq, Hkv=Hkv, D=D, Di=Di, P=P, MB=MB, k=k, B=B,
+                fp8=fp8, seq_lens=torch.from_numpy(lens.astype(np.int32)),
+                block_table=torch.from_numpy(bt), q_idx=q_idx, index_k=index_k,
+                q=q, k_cache=k_cache, v_cache=v_cache, idx_scale=idx_scale,
+                k_scale=k_scale, v_scale=v_scale, sm_scale=sm_scale)
+
+
+# ---------------------------------------------------------------- named workloads
+
+def tiny(seed: int = 1000) -> Case:
+    """fp32, 1 row x 1 token, 4 q heads / 1 KV head, D=64, Di=32, 1024 tokens
+    (8 blocks) mapped into a 16-page pool, top-k 4, all scales 1.0."""
+    c = make_case("tiny_fp32", R=1, T=1, Hq=4, Hkv=1, D=64, Di=32, seq_lens=[1024],
+                  P=16, k=4, fp8=False, seed=seed)
+    c.sm_scale = 0.125
+    return c
+
+
+def decode_bucket4(seed: int = 2000) -> Case:
+    """4 rows x 4 tokens, 16 q heads / 1 KV head, D=Di=128, FP8 caches, 16384
+    context (128 blocks), top-k 16, 1024-page pool with a random block table."""
+    return make_case("decode_r4_16k", R=4, T=4, Hq=16, Hkv=1, D=128, Di=128,
+                     seq_lens=[16384] * 4, P=1024, k=16, seed=seed)
+
+
+def bucket_sweep(R: int, seed: Optional[int] = None, pad_rows: Sequence[int] = ()) -> Case:
+    """R rows x 4 tokens, per-row lengths uniform in [2048, 16384], top-k 16,
+    4096-page pool, MB=128.  ``pad_rows`` get seq_len 0 and NaN queries."""
+    seed = 3000 + R if seed is None else seed
+    g = _rng(seed, "lens")
+    lens = g.integers(2048, 16384, size=R, endpoint=True)
+    for r in pad_rows:
+        lens[r] = 0
+    return make_case(f"sweep_r{R}", R=R, T=4, Hq=16, Hkv=1, D=128, Di=128,
+                     seq_lens=lens.tolist(), P=4096, k=16, MB=128, seed=seed,
+                     nan_q_rows=pad_rows)
+
+
+def prefill(seed: int = 4000) -> Case:
+    """4 requests x 2048 new tokens over an 8192-token prefix (seq_len 10240,
+    80 blocks), FP8 index dim 128, per-token top-k 16 -> topk [8192, 16]."""
+    return make_case("prefill_4x2048", R=4, T=2048, Hq=16, Hkv=1, D=128, Di=128,
+                     seq_lens=[10240] * 4, P=1024, k=16, seed=seed, attention=False)
+
+
+def hbm_decode(k: int = 16, seed: Optional[int] = None) -> Case:
+    """16 rows x 4 tokens at 16384 context, 16 q / 1 KV heads, D=Di=128, FP8
+    caches, 4096-page pool with non-overlapping tables, top-k ``k``."""
+    seed = 5000 + k if seed is None else seed
+    return make_case(f"hbm_r16_16k_k{k}", R=16, T=4, Hq=16, Hkv=1, D=128, Di=128,
+                     seq_lens=[16384] * 16, P=4096, k=k, seed=seed)
+
+
+def small_fp8(R: int = 2, T: int = 4, lens: Sequence[int] = (700, 1500), k: int = 4,
+              P: Optional[int] = None, Hq: int = 16, D: int = 128, Di: int = 128,
+              seed: int = 7, **kw) -> Case:
+    """A small FP8 case spanning several blocks with ragged tails."""
+    nblk = sum((int(x) + BLOCK - 1) // BLOCK for x in lens)
+    P = P if P is not None else nblk + 5
+    return make_case(f"small_fp8_r{R}", R=R, T=T, Hq=Hq, Hkv=1, D=D, Di=Di,
+                     seq_lens=list(lens), P=P, k=k, seed=seed, **kw)
+
+
+def random_topk(case: Case, seed: int = 11) -> torch.Tensor:
+    """Caller-style topk_idx [N, k]: each token draws k distinct visible blocks
+    (ascending, -1 padded) -- for testing attention on its own."""
+    g = _rng(seed, "topk")
+    out = np.full((case.N, case.k), -1, dtype=np.int32)
+    for n in range(case.N):
+        nvis = (case.visible(n) + case.B - 1) // case.B
+        m = min(case.k, nvis)
+        if m:
+            out[n, :m] = np.sort(g.choice(nvis, size=m, replace=False))
+    return torch.from_numpy(out)

@@ -1,0 +1,388 @@
+"""Pins for the CPU oracle (no GPU).
+
+The oracle is checked against things other than itself:
+  * library routines: torch's float8_e4m3fn / bfloat16 casts for the decoders;
+  * hand-worked examples under tests/golden/ (each with its citation);
+  * closed forms: one-hot and constant inputs, single visible key, equal keys,
+    sm_scale = 0, value scaling;
+  * brute force on tiny inputs by a structurally different route (a dense
+    masked [N, L] matrix built with numpy matmul, reshaped per block);
+  * invariants: top-k with every block selected equals dense attention,
+    permuting physical pages together with the block table changes nothing,
+    selections are the k best with ties to the lower id.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _f(x):
+    if x is None:
+        return float("nan")
+    if isinstance(x, str):
+        return float(x)
+    return float(x)
+
+
+def _arr(nested):
+    return np.vectorize(_f, otypes=[np.float64])(np.array(nested, dtype=object))
+
+
+# ------------------------------------------------------------------ decoding
+
+def test_e4m3fn_all_codes_match_torch(orc):
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    got = np.array([orc.e4m3fn_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def test_e4m3fn_spec_codes(orc):
+    g = json.load(open(os.path.join(GOLDEN, "e4m3fn_codes.json")))
+    for k, v in g["codes"].items():
+        got = orc.e4m3fn_value(int(k, 16))
+        if v == "nan":
+            assert math.isnan(got), k
+        else:
+            assert got == v and math.copysign(1, got) == math.copysign(1, v), k
+
+
+def test_bf16_all_patterns_match_torch(orc):
+    bits = torch.arange(-32768, 32768, dtype=torch.int32).to(torch.int16)
+    ref = bits.view(torch.bfloat16).to(torch.float32).double().numpy()
+    sample = np.arange(0, 65536, 7)   # every 7th pattern through the C entry point
+    got = np.array([orc.bf16_value(int(bits[i]) & 0xFFFF) for i in sample])
+    r = ref[sample]
+    assert np.array_equal(np.isnan(r), np.isnan(got))
+    ok = ~np.isnan(r)
+    assert np.array_equal(r[ok], got[ok])
+
+
+# ------------------------------------------------------------ brute force
+
+def _decode(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.uint8:
+        return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    return t.to(torch.float64).numpy()
+
+
+def _dense_keys(case, pool, r):
+    """All key positions of row r in order, gathered through the block table."""
+    arr = _decode(pool)
+    L = int(case.seq_lens[r])
+    pages = case.block_table[r].numpy()
+    idx = np.arange(L)
+    return arr[pages[idx // case.B], idx % case.B]
+
+
+def brute_scores(case):
+    """score[n, j] via a dense masked dot matrix per row, reshaped into blocks."""
+    qi = _decode(case.q_idx)
+    N, MB, B = case.N, case.MB, case.B
+    out = np.full((N, MB), -np.inf)
+    for r in range(case.R):
+        L = int(case.seq_lens[r])
+        if L == 0:
+            continue
+        K = _dense_keys(case, case.index_k, r)                 # [L, Di]
+        rows = slice(r * case.T, (r + 1) * case.T)
+        dots = qi[rows] @ K.T                                  # [T, L]
+        vis = np.array([case.visible(n) for n in range(r * case.T, (r + 1) * case.T)])
+        dots = np.where(np.arange(L)[None, :] < vis[:, None], dots, -np.inf)
+        pad = MB * B - L
+        dots = np.concatenate([dots, np.full((case.T, pad), -np.inf)], axis=1)
+        out[rows] = dots.reshape(case.T, MB, B).max(axis=2) * case.idx_scale
+    return out
+
+
+def brute_attention(case, topk):
+    """Masked dense softmax over [N, Hq, L] built from numpy matmuls."""
+    q = _decode(case.q)
+    N, Hq, D = q.shape
+    G = case.Hq // case.Hkv
+    out = np.zeros((N, Hq, D))
+    for r in range(case.R):
+        L = int(case.seq_lens[r])
+        if L == 0:
+            continue
+        Kf = _dense_keys(case, case.k_cache, r) * case.k_scale   # [L, Hkv, D]
+        Vf = _dense_keys(case, case.v_cache, r) * case.v_scale
+        for t in range(case.T):
+            n = r * case.T + t
+            sel = np.zeros(L, dtype=bool)
+            for j in topk[n]:
+                if 0 <= j < case.MB:
+                    sel[j * case.B:(j + 1) * case.B] = True
+            sel &= np.arange(L) < case.visible(n)
+            if not sel.any():
+                continue
+            for h in range(Hq):
+                g = h // G
+                logits = case.sm_scale * (Kf[sel, g] @ q[n, h])
+                w = np.exp(logits - logits.max())
+                out[n, h] = (w / w.sum()) @ Vf[sel, g]
+    return out
+
+
+def small_cases():
+    return [
+        synth.make_case("b4_fp32", R=2, T=3, Hq=4, Hkv=2, D=8, Di=4, seq_lens=[13, 7], P=12,
+                        k=2, fp8=False, seed=1, B=4),
+        synth.make_case("b4_fp8", R=3, T=4, Hq=4, Hkv=1, D=16, Di=8, seq_lens=[17, 3, 0],
+                        P=14, k=3, fp8=True, seed=2, B=4),
+        synth.make_case("b8_fp8_shared", R=2, T=2, Hq=2, Hkv=1, D=8, Di=8, seq_lens=[30, 25],
+                        P=9, k=2, fp8=True, seed=3, B=8, shared_pages=True),
+        synth.make_case("b128_fp8", R=1, T=4, Hq=16, Hkv=1, D=32, Di=32, seq_lens=[300],
+                        P=6, k=2, fp8=True, seed=4),
+    ]
+
+
+@pytest.mark.parametrize("case", small_cases(), ids=lambda c: c.name)
+def test_score_matches_brute_force(orc, case):
+    got = orc.block_score(case.q_idx, case.index_k, case.block_table, case.seq_lens, case.T,
+                          case.idx_scale)
+    ref = brute_scores(case)
+    assert np.array_equal(np.isinf(got), np.isinf(ref))
+    fin = np.isfinite(ref)
+    np.testing.assert_allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", small_cases(), ids=lambda c: c.name)
+def test_attention_matches_brute_force(orc, case):
+    topk = synth.random_topk(case, seed=5).numpy()
+    got = orc.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                            topk, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    ref = brute_attention(case, topk)
+    np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", small_cases(), ids=lambda c: c.name)
+def test_all_blocks_selected_equals_dense(orc, case):
+    topk = np.tile(np.arange(case.MB, dtype=np.int32), (case.N, 1))
+    sparse = orc.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table,
+                               case.seq_lens, topk, case.T, case.sm_scale, case.k_scale,
+                               case.v_scale)
+    dense = orc.dense_attention(case.q, case.k_cache, case.v_cache, case.block_table,
+                                case.seq_lens, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    np.testing.assert_allclose(sparse, dense, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(dense, brute_attention(case, topk), rtol=1e-11, atol=1e-12)
+
+
+def test_select_matches_brute_force(orc):
+    g = np.random.default_rng(9)
+    for trial in range(200):
+        MB = int(g.integers(1, 40))
+        k = int(g.integers(1, 45))
+        vals = g.choice([-1.0, 0.0, -0.0, 1.0, 2.5, np.inf, -np.inf, np.nan, 3.0], size=MB)
+        vals = np.where(g.random(MB) < 0.5, g.normal(size=MB).round(1), vals)
+        got = orc.select_topk(vals[None, :], k)[0]
+        cand = [(0.0 if v == 0 else v, j) for j, v in enumerate(vals)
+                if not (np.isnan(v) or v == -np.inf)]
+        best = sorted(cand, key=lambda x: (-x[0], x[1]))[:k]
+        want = sorted(j for _, j in best)
+        want = want + [-1] * (k - len(want))
+        assert got.tolist() == want, (vals, k)
+
+
+def test_select_invariants(orc):
+    MB = 32
+    eq = orc.select_topk(np.full((1, MB), 1.5), 5)[0]
+    assert eq.tolist() == [0, 1, 2, 3, 4]                       # ties -> lower ids
+    inc = orc.select_topk(np.arange(MB, dtype=np.float64)[None], 4)[0]
+    assert inc.tolist() == [28, 29, 30, 31]
+    few = np.full((1, MB), -np.inf)
+    few[0, [3, 17]] = [2.0, -5.0]
+    assert orc.select_topk(few, 4)[0].tolist() == [3, 17, -1, -1]
+    z = np.array([[-0.0, 0.0, -0.0]])
+    assert orc.select_topk(z, 1)[0].tolist() == [0]            # -0 equals +0
+    g = np.random.default_rng(3)
+    s = g.normal(size=(50, MB))
+    tk = orc.select_topk(s, 7)
+    for n in range(50):
+        sel = s[n, tk[n]]
+        rest = np.delete(s[n], tk[n])
+        assert sel.min() >= rest.max()
+        assert np.all(np.diff(tk[n]) > 0)
+
+
+# ------------------------------------------------------------ closed forms
+
+def test_score_one_hot_query(orc):
+    case = small_cases()[1]
+    for d in range(case.Di):
+        qi = torch.zeros_like(case.q_idx, dtype=torch.float32)
+        qi[:, d] = 1.0
+        got = orc.block_score(qi, case.index_k, case.block_table, case.seq_lens, case.T,
+                              case.idx_scale)
+        codes = _decode(case.index_k)
+        for n in range(case.N):
+            r = n // case.T
+            vis = case.visible(n)
+            for j in range(case.MB):
+                lo, hi = j * case.B, min((j + 1) * case.B, vis)
+                if lo >= hi:
+                    assert got[n, j] == -np.inf
+                    continue
+                col = codes[int(case.block_table[r, j]), : hi - lo, d]
+                assert got[n, j] == col.max() * case.idx_scale
+
+
+def test_score_constant_codes(orc):
+    case = small_cases()[1]
+    idx = torch.full_like(case.index_k, 0x40)           # every code = 2.0
+    got = orc.block_score(case.q_idx, idx, case.block_table, case.seq_lens, case.T,
+                          case.idx_scale)
+    qsum = _decode(case.q_idx).sum(axis=1)
+    for n in range(case.N):
+        for j in range(case.MB):
+            if j * case.B < case.visible(n):
+                assert got[n, j] == pytest.approx(2.0 * qsum[n] * case.idx_scale, rel=1e-13)
+            else:
+                assert got[n, j] == -np.inf
+
+
+def test_score_causal_offset(orc):
+    """Token t of a row sees exactly seq_len - (T-1-t) keys."""
+    case = synth.make_case("causal", R=1, T=4, Hq=2, Hkv=1, D=4, Di=4, seq_lens=[10], P=4, k=1,
+                           fp8=False, seed=1, B=4)
+    idx = case.index_k.clone()
+    qi = torch.zeros(4, 4)
+    qi[:, 0] = 1.0
+    for s in range(10):                                 # key s has value s in dim 0
+        idx[int(case.block_table[0, s // 4]), s % 4, 0] = float(s)
+    got = orc.block_score(qi, idx, case.block_table, case.seq_lens, 4, 1.0)
+    # visible counts 7, 8, 9, 10 -> last visible key 6, 7, 8, 9 (block 1 or 2)
+    assert got[0].tolist() == [3.0, 6.0, -np.inf]
+    assert got[1].tolist() == [3.0, 7.0, -np.inf]
+    assert got[2].tolist() == [3.0, 7.0, 8.0]
+    assert got[3].tolist() == [3.0, 7.0, 9.0]
+
+
+def test_golden_score_select(orc):
+    g = json.load(open(os.path.join(GOLDEN, "score_select_hand.json")))
+    idx = torch.tensor(_arr(g["index_k"]), dtype=torch.float32)
+    qi = torch.tensor(g["q_idx"], dtype=torch.float32)
+    bt = torch.tensor(g["block_table"], dtype=torch.int32)
+    sl = torch.tensor(g["seq_lens"], dtype=torch.int32)
+    got = orc.block_score(qi, idx, bt, sl, g["T"], g["idx_scale"])
+    want = _arr(g["scores"])
+    assert np.array_equal(got, want)
+    assert orc.select_topk(got, 1).tolist() == g["topk1"]
+    assert orc.select_topk(got, 2).tolist() == g["topk2"]
+
+
+def test_golden_attention(orc):
+    g = json.load(open(os.path.join(GOLDEN, "attention_hand.json")))
+    kc = torch.tensor(_arr(g["k_cache"]), dtype=torch.float32)
+    vc = torch.tensor(_arr(g["v_cache"]), dtype=torch.float32)
+    q = torch.tensor(g["q"], dtype=torch.float32)
+    bt = torch.tensor(g["block_table"], dtype=torch.int32)
+    sl = torch.tensor(g["seq_lens"], dtype=torch.int32)
+    for c in g["cases"]:
+        got = orc.sparse_decode(q, kc, vc, bt, sl, np.array(c["topk"], dtype=np.int32), g["T"],
+                                math.log(2.0), 1.0, 1.0)
+        np.testing.assert_allclose(got, np.array(c["out"]), rtol=1e-14, atol=1e-14)
+
+
+def _attn(orc, case, topk, **kw):
+    a = dict(sm_scale=case.sm_scale, k_scale=case.k_scale, v_scale=case.v_scale)
+    a.update(kw)
+    return orc.sparse_decode(kw.pop("q", case.q), kw.pop("k_cache", case.k_cache),
+                             kw.pop("v_cache", case.v_cache), case.block_table, case.seq_lens,
+                             topk, case.T, a["sm_scale"], a["k_scale"], a["v_scale"])
+
+
+def test_attention_closed_forms(orc):
+    case = synth.make_case("cf", R=1, T=1, Hq=4, Hkv=1, D=8, Di=4, seq_lens=[9], P=5, k=3,
+                           fp8=True, seed=8, B=4)
+    topk = np.array([[0, 2, -1]], dtype=np.int32)          # keys 0..3 and 8
+    v = _decode(case.v_cache)
+    kc = _decode(case.k_cache)
+    pg = case.block_table[0].numpy()
+    keys = [(pg[0], s) for s in range(4)] + [(pg[2], 0)]
+    base = _attn(orc, case, topk)
+    # v_scale doubles -> output doubles exactly
+    twice = _attn(orc, case, topk, v_scale=2 * case.v_scale)
+    assert np.array_equal(twice, 2 * base)
+    # sm_scale = 0 -> plain mean of the selected visible values
+    uni = _attn(orc, case, topk, sm_scale=0.0)
+    mean = np.mean([v[p, s, 0] for p, s in keys], axis=0) * case.v_scale
+    for h in range(4):
+        np.testing.assert_allclose(uni[0, h], mean, rtol=1e-13)
+    # one visible key (block 2 holds only key 8) -> exactly that value
+    one = _attn(orc, case, np.array([[2, -1, -1]], dtype=np.int32))
+    for h in range(4):
+        assert np.array_equal(one[0, h], v[pg[2], 0, 0] * case.v_scale)
+    # identical keys -> weights equal -> mean of the values
+    kk = case.k_cache.clone()
+    for p, s in keys:
+        kk[p, s] = case.k_cache[pg[0], 0]
+    same = orc.sparse_decode(case.q, kk, case.v_cache, case.block_table, case.seq_lens, topk,
+                             case.T, case.sm_scale, case.k_scale, case.v_scale)
+    for h in range(4):
+        np.testing.assert_allclose(same[0, h], mean, rtol=1e-13)
+    # constant values -> that constant whatever the weights
+    vv = case.v_cache.clone()
+    vv[:] = 0x38                                          # code 1.0
+    const = orc.sparse_decode(case.q, case.k_cache, vv, case.block_table, case.seq_lens, topk,
+                              case.T, case.sm_scale, case.k_scale, case.v_scale)
+    np.testing.assert_allclose(const, case.v_scale, rtol=1e-14)
+    assert np.isfinite(kc[pg[0]]).all()
+
+
+def test_attention_empty_and_invalid_ids(orc):
+    case = small_cases()[1]                              # row 2 has seq_len 0
+    topk = np.full((case.N, case.k), -1, dtype=np.int32)
+    out = _attn(orc, case, topk)
+    assert np.array_equal(out, np.zeros_like(out))
+    tk = synth.random_topk(case, seed=3).numpy()
+    base = _attn(orc, case, tk)
+    odd = tk.copy()
+    odd[odd == -1] = case.MB + 7                          # out-of-range ids count as none
+    assert np.array_equal(_attn(orc, case, odd), base)
+    dup = tk.copy()
+    dup[0, 1] = dup[0, 0]
+    with pytest.raises(Exception):
+        _attn(orc, case, dup)
+
+
+def test_page_permutation_invariance(orc):
+    case = small_cases()[1]
+    g = np.random.default_rng(12)
+    perm = g.permutation(case.P)                          # new page of old page p = perm[p]
+    inv = np.argsort(perm)
+
+    def move(pool):
+        return pool[torch.from_numpy(inv)]
+
+    bt2 = torch.from_numpy(perm[case.block_table.numpy()].astype(np.int32))
+    s1 = orc.block_score(case.q_idx, case.index_k, case.block_table, case.seq_lens, case.T,
+                         case.idx_scale)
+    s2 = orc.block_score(case.q_idx, move(case.index_k), bt2, case.seq_lens, case.T,
+                         case.idx_scale)
+    assert np.array_equal(s1, s2)
+    tk = orc.select_topk(s1, case.k)
+    o1 = orc.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                           tk, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    o2 = orc.sparse_decode(case.q, move(case.k_cache), move(case.v_cache), bt2, case.seq_lens,
+                           tk, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    assert np.array_equal(o1, o2)
+
+
+def test_round_bf16_matches_torch(orc):
+    g = np.random.default_rng(1)
+    x = np.concatenate([g.normal(size=5000) * 0.05, g.normal(size=5000) * 30])
+    x32 = x.astype(np.float32).astype(np.float64)      # exactly representable in f32
+    ref = torch.from_numpy(x32).to(torch.float32).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(orc.round_bf16(x32), ref)
