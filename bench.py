@@ -1,0 +1,236 @@
+"""Throughput of the MSA sparse-layer decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch: block scores over the
+FP8 index cache, top-k block selection, and sparse attention over the selected
+FP8 K/V pages with its split-K merge -- the three C-ABI calls back to back on
+one stream.  Workload: 16 request rows x 4 query tokens (1 + 3 speculative),
+16384-token context per row (128 blocks of 128), 16 query heads / 1 KV head,
+head dim 128, index dim 128, top-k 16, a 4096-page pool with random
+non-overlapping block tables (synthetic seeded data).
+
+Timing: M independent copies of the pools (192 MiB each) are rotated so that
+each step reads cold data rather than the 256 MB Infinity Cache; M steps are
+captured into one HIP graph, replayed after warm-up, and bracketed by HIP
+events after a device synchronisation.  The per-kernel durations used for the
+roofline come from graphs of M back-to-back launches of each call, timed the
+same way on the same stream.  The CPU baseline is the oracle (plain C, fp64)
+running one full step of the same batch on the host cores.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--k", type=int, default=16)
+    ap.add_argument("--copies", type=int, default=8, help="pool copies rotated per graph")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernels", default="score,select,decode",
+                    help="per-call timing graphs to build")
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "block_sparse_paged_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(case, topk: np.ndarray) -> dict:
+    """Bytes each call must move at minimum (each touched page once per row)."""
+    R, T, N, MB, B = case.R, case.T, case.N, case.MB, case.B
+    lens = case.seq_lens.numpy().astype(np.int64)
+    Di, D, Hq, Hkv, k = case.Di, case.D, case.Hq, case.Hkv, topk.shape[1]
+    index = int(lens.sum()) * Di * 1
+    kv_tokens = 0
+    for r in range(R):
+        ids = np.unique(topk[r * T:(r + 1) * T])
+        ids = ids[ids >= 0]
+        kv_tokens += int(sum(min(B, lens[r] - j * B) for j in ids if j * B < lens[r]))
+    kv = kv_tokens * Hkv * D * 1 * 2
+    small_bt = R * MB * 4 + R * 4
+    score = index + N * Di * 2 + N * MB * 4 + small_bt
+    select = N * MB * 4 + N * k * 4
+    attend = kv + N * Hq * D * 2 + N * k * 4 + small_bt
+    reduce_ = N * Hq * D * 2
+    return dict(score=score, select=select, attend=attend, reduce=reduce_,
+                decode=attend + reduce_, step=score + select + attend + reduce_,
+                index=index, kv=kv)
+
+
+def cpu_baseline(case) -> dict:
+    import oracle
+    try:
+        threads = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    s = oracle.block_score(case.q_idx, case.index_k, case.block_table, case.seq_lens, case.T,
+                           case.idx_scale, threads=threads)
+    tk = oracle.select_topk(s, case.k)
+    oracle.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens, tk,
+                         case.T, case.sm_scale, case.k_scale, case.v_scale, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(1.0 / dt, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"one full step of the same {case.R}x{case.T}-token batch "
+                      f"(score+select+attend, fp64 C, {threads} threads), {dt:.2f} s wall"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
+              "(the sharded path is described, not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import block_sparse_paged_amd as msa
+    import synth
+
+    case = synth.hbm_decode(a.k)
+    M = max(1, a.copies)
+    dev = "cuda"
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    q_idx = case.q_idx.to(dev)
+    q = case.q.to(dev)
+    bt = case.block_table.to(dev)
+    sl = case.seq_lens.to(dev)
+    pools = []
+    idx0, k0, v0 = f8(case.index_k).to(dev), f8(case.k_cache).to(dev), f8(case.v_cache).to(dev)
+    for i in range(M):
+        pools.append((idx0.clone(), k0.clone(), v0.clone()) if i else (idx0, k0, v0))
+    scores = [torch.full((case.N, case.MB), float("nan"), device=dev) for _ in range(M)]
+    topk = [torch.full((case.N, case.k), -1, dtype=torch.int32, device=dev) for _ in range(M)]
+    out = [torch.full((case.N, case.Hq, case.D), float("nan"), dtype=torch.bfloat16, device=dev)
+           for _ in range(M)]
+    wsb = msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, case.k)
+    ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(M)]
+
+    def call(name, i):
+        idx, kc, vc = pools[i]
+        if name == "score":
+            msa.msa_block_score(q_idx, idx, bt, sl, case.T, case.B, case.idx_scale, scores[i])
+        elif name == "select":
+            msa.msa_select_topk(scores[i], case.k, topk[i])
+        else:
+            msa.msa_sparse_decode(q, kc, vc, bt, sl, topk[i], case.T, out[i], case.sm_scale,
+                                  case.k_scale, case.v_scale, case.B, ws[i])
+
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(M):
+            for name in ("score", "select", "decode"):
+                call(name, i)
+    torch.cuda.synchronize()
+
+    def capture(names):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(M):
+                for name in names:
+                    call(name, i)
+        return g
+
+    step_graph = capture(("score", "select", "decode"))
+    reps_w = max(1, a.warmup // M)
+    reps = max(1, a.steps // M)
+    steps = reps * M
+
+    def timed(g, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(n):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1000.0   # seconds
+
+    with torch.cuda.stream(stream):
+        for _ in range(reps_w):
+            step_graph.replay()
+    torch.cuda.synchronize()
+    t_step = timed(step_graph, reps) / steps
+
+    per_call = {}
+    for name in [n for n in a.kernels.split(",") if n]:
+        g = capture((name,))
+        with torch.cuda.stream(stream):
+            for _ in range(max(1, reps_w // 4)):
+                g.replay()
+        per_call[name] = timed(g, max(1, reps // 2)) / (max(1, reps // 2) * M)
+        del g
+
+    tk_host = topk[0].cpu().numpy()
+    ab = algorithmic_bytes(case, tk_host)
+    eff_gbs = ab["step"] / t_step / 1e9
+    # dominant call: the one with the longest launch duration
+    dom = max(per_call, key=per_call.get) if per_call else "decode"
+    dom_bytes = ab[dom]
+    dom_gbs = dom_bytes / per_call.get(dom, t_step) / 1e9
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "traffic.json")
+    if os.path.exists(tfile):
+        try:
+            tj = json.load(open(tfile))
+            if tj.get("source_digest") == kernel_source_digest() and dom in tj.get("calls", {}):
+                traffic = tj["calls"][dom]
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "sparse decode steps/s + achieved HBM GB/s (% of peak), 16 rows x 16K ctx",
+        "value": round(1.0 / t_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": reps_w * M,
+        "ms_per_step": round(t_step * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3-in/bf16-mfma/fp32-acc",
+        "data": "synthetic (seeded N(0,1), per-tensor E4M3 quantised, random page tables)",
+        "config": {"workload": "msa sparse decode step, 16 rows x 4 tokens, 16384 ctx, "
+                               "16q/1kv heads, D=Di=128, FP8 caches, top-k 16",
+                   "rows": case.R, "tokens_per_row": case.T, "context": int(case.seq_lens[0]),
+                   "top_k": case.k, "pool_pages": case.P, "pool_copies": M},
+        "achieved_hbm_gbs": round(eff_gbs, 1),
+        "pct_of_hbm_peak": round(100.0 * eff_gbs / HBM_PEAK_GBS, 2),
+        "algorithmic_bytes_per_step": ab["step"],
+        "per_call_us": {k: round(v * 1e6, 3) for k, v in per_call.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "algorithmic_bytes": dom_bytes},
+    }
+    if not a.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,265 @@
+// C ABI entry points (declared in include/msa.h): descriptor validation on the
+// host, then kernel launches on the caller's stream.  Nothing here allocates,
+// synchronises or keeps a pointer past the call.
+#include <math.h>
+#include <string.h>
+
+#include "msa.h"
+#include "msa_internal.h"
+
+using namespace msa;
+
+namespace {
+
+thread_local int32_t g_last_error = MSA_OK;
+
+void set_error(int32_t e) { g_last_error = e; }
+
+struct Check {
+    int32_t err = MSA_OK;
+    bool ok() const { return err == MSA_OK; }
+    void fail(int32_t e) {
+        if (err == MSA_OK) err = e;
+    }
+};
+
+int esize(int32_t dt) {
+    switch (dt) {
+    case MSA_F32: return 4;
+    case MSA_BF16: return 2;
+    case MSA_FP8_E4M3FN: return 1;
+    case MSA_I32: return 4;
+    }
+    return 0;
+}
+
+// Basic descriptor sanity: non-null, ndim, non-negative sizes and strides.
+void desc(Check &c, const msa_tensor *t, int ndim) {
+    if (!t) { c.fail(MSA_ERR_NULL); return; }
+    if (t->ndim != ndim) { c.fail(MSA_ERR_SHAPE); return; }
+    int64_t numel = 1;
+    for (int i = 0; i < ndim; ++i) {
+        if (t->shape[i] < 0 || t->stride[i] < 0) { c.fail(MSA_ERR_SHAPE); return; }
+        numel *= t->shape[i];
+    }
+    if (numel > 0 && !t->data) c.fail(MSA_ERR_NULL);
+}
+
+void dtype_in(Check &c, const msa_tensor *t, std::initializer_list<int32_t> ok) {
+    if (!t) return;
+    for (int32_t d : ok)
+        if (t->dtype == d) return;
+    c.fail(MSA_ERR_DTYPE);
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Innermost stride 1; the other strides and the base keep 16-byte rows aligned.
+void rows16(Check &c, const msa_tensor *t) {
+    if (!t || t->ndim < 1) return;
+    const int es = esize(t->dtype);
+    if (t->stride[t->ndim - 1] != 1 && t->shape[t->ndim - 1] > 1) { c.fail(MSA_ERR_LAYOUT); return; }
+    if (!aligned16(t->data)) { c.fail(MSA_ERR_LAYOUT); return; }
+    for (int i = 0; i < t->ndim - 1; ++i)
+        if (t->shape[i] > 1 && ((t->stride[i] * es) & 15)) { c.fail(MSA_ERR_LAYOUT); return; }
+}
+
+bool fits_i32(int64_t x) { return x >= 0 && x <= 0x7fffffff; }
+
+int etype(int32_t dt) {
+    switch (dt) {
+    case MSA_F32: return E_F32;
+    case MSA_BF16: return E_BF16;
+    case MSA_FP8_E4M3FN: return E_FP8;
+    }
+    return E_I32;
+}
+
+// Shared checks of block_table [R, MB] and seq_lens [R].
+void paging(Check &c, const msa_tensor *bt, const msa_tensor *sl) {
+    desc(c, bt, 2);
+    desc(c, sl, 1);
+    dtype_in(c, bt, {MSA_I32});
+    dtype_in(c, sl, {MSA_I32});
+    if (!c.ok()) return;
+    if (sl->shape[0] != bt->shape[0]) c.fail(MSA_ERR_SHAPE);
+    if (bt->shape[1] < 1 || bt->shape[1] > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t msa_get_last_error(void) {
+    const int32_t e = g_last_error;
+    g_last_error = MSA_OK;
+    return e;
+}
+
+const char *msa_error_string(int32_t code) {
+    switch (code) {
+    case MSA_OK: return "no error";
+    case MSA_ERR_NULL: return "a required pointer is NULL";
+    case MSA_ERR_DTYPE: return "dtype outside the supported set";
+    case MSA_ERR_SHAPE: return "tensor rank or sizes disagree";
+    case MSA_ERR_LAYOUT: return "innermost stride must be 1 with 16-byte aligned rows";
+    case MSA_ERR_UNSUPPORTED: return "size outside the supported domain";
+    case MSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MSA_ERR_ARG: return "scalar argument out of range";
+    case MSA_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown error";
+}
+
+void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
+                     const msa_tensor *block_table, const msa_tensor *seq_lens,
+                     int32_t tokens_per_row, int32_t block_size, float idx_scale,
+                     msa_tensor *scores, hipStream_t stream) {
+    Check c;
+    desc(c, q_idx, 2);
+    desc(c, index_k, 3);
+    desc(c, scores, 2);
+    paging(c, block_table, seq_lens);
+    dtype_in(c, q_idx, {MSA_BF16, MSA_F32});
+    dtype_in(c, index_k, {MSA_FP8_E4M3FN, MSA_F32});
+    dtype_in(c, scores, {MSA_F32});
+    if (!c.ok()) { set_error(c.err); return; }
+    if (block_size != kBlock) c.fail(MSA_ERR_UNSUPPORTED);
+    if (tokens_per_row < 1) c.fail(MSA_ERR_ARG);
+    if (!(idx_scale > 0.f) || !isfinite(idx_scale)) c.fail(MSA_ERR_ARG);
+    const int64_t R = block_table->shape[0], MB = block_table->shape[1];
+    const int64_t N = R * (int64_t)tokens_per_row;
+    const int64_t Di = q_idx->shape[1];
+    if (q_idx->shape[0] != N || scores->shape[0] != N || scores->shape[1] != MB) c.fail(MSA_ERR_SHAPE);
+    if (index_k->shape[1] != kBlock || index_k->shape[2] != Di) c.fail(MSA_ERR_SHAPE);
+    if (!score_supported(etype(q_idx->dtype), etype(index_k->dtype), (int)Di)) c.fail(MSA_ERR_UNSUPPORTED);
+    if (!fits_i32(N) || !fits_i32(index_k->shape[0])) c.fail(MSA_ERR_UNSUPPORTED);
+    rows16(c, q_idx);
+    rows16(c, index_k);
+    if (!c.ok()) { set_error(c.err); return; }
+    if (N == 0) return;
+
+    ScoreParams p{};
+    p.q_idx = q_idx->data; p.q_sn = q_idx->stride[0];
+    p.index_k = index_k->data; p.k_sp = index_k->stride[0]; p.k_sb = index_k->stride[1];
+    p.bt = (const int32_t *)block_table->data;
+    p.bt_sr = block_table->stride[0]; p.bt_sj = block_table->stride[1];
+    p.seq_lens = (const int32_t *)seq_lens->data; p.sl_s = seq_lens->stride[0];
+    p.scores = (float *)scores->data; p.sc_sn = scores->stride[0]; p.sc_sj = scores->stride[1];
+    p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB;
+    p.P = (int32_t)index_k->shape[0];
+    p.idx_scale = idx_scale;
+    if (launch_score(p, etype(q_idx->dtype), etype(index_k->dtype), (int)Di, stream) != hipSuccess)
+        set_error(MSA_ERR_LAUNCH);
+}
+
+void msa_select_topk(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
+                     hipStream_t stream) {
+    Check c;
+    desc(c, scores, 2);
+    desc(c, topk_idx, 2);
+    dtype_in(c, scores, {MSA_F32});
+    dtype_in(c, topk_idx, {MSA_I32});
+    if (!c.ok()) { set_error(c.err); return; }
+    const int64_t N = scores->shape[0], MB = scores->shape[1];
+    if (MB < 1 || MB > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
+    if (k < 1 || k > MB) c.fail(MSA_ERR_ARG);
+    if (topk_idx->shape[0] != N || topk_idx->shape[1] != k) c.fail(MSA_ERR_SHAPE);
+    if (!fits_i32(N)) c.fail(MSA_ERR_UNSUPPORTED);
+    if (!c.ok()) { set_error(c.err); return; }
+    if (N == 0) return;
+    TopkParams p{};
+    p.scores = (const float *)scores->data; p.sc_sn = scores->stride[0]; p.sc_sj = scores->stride[1];
+    p.topk = (int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
+    p.N = (int32_t)N; p.MB = (int32_t)MB; p.k = k;
+    if (launch_topk(p, stream) != hipSuccess) set_error(MSA_ERR_LAUNCH);
+}
+
+size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t k) {
+    if (rows < 0 || tokens_per_row < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1 || k < 1)
+        return 0;
+    return attn_workspace_bytes(rows, tokens_per_row, num_q_heads, num_kv_heads, head_dim, k);
+}
+
+void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
+                       const msa_tensor *v_cache, const msa_tensor *block_table,
+                       const msa_tensor *seq_lens, const msa_tensor *topk_idx,
+                       int32_t tokens_per_row, msa_tensor *out,
+                       float sm_scale, float k_scale, float v_scale, int32_t block_size,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Check c;
+    desc(c, q, 3);
+    desc(c, k_cache, 4);
+    desc(c, v_cache, 4);
+    desc(c, topk_idx, 2);
+    desc(c, out, 3);
+    paging(c, block_table, seq_lens);
+    dtype_in(c, q, {MSA_BF16, MSA_F32});
+    dtype_in(c, k_cache, {MSA_FP8_E4M3FN, MSA_F32});
+    dtype_in(c, topk_idx, {MSA_I32});
+    dtype_in(c, out, {MSA_BF16, MSA_F32});
+    if (!c.ok()) { set_error(c.err); return; }
+    if (v_cache->dtype != k_cache->dtype) c.fail(MSA_ERR_DTYPE);
+    if (block_size != kBlock) c.fail(MSA_ERR_UNSUPPORTED);
+    if (tokens_per_row < 1) c.fail(MSA_ERR_ARG);
+    if (!isfinite(sm_scale) || !isfinite(k_scale) || !isfinite(v_scale)) c.fail(MSA_ERR_ARG);
+    const int64_t R = block_table->shape[0], MB = block_table->shape[1];
+    const int64_t N = R * (int64_t)tokens_per_row;
+    const int64_t Hq = q->shape[1], D = q->shape[2];
+    const int64_t P = k_cache->shape[0], Hkv = k_cache->shape[2];
+    const int64_t K = topk_idx->shape[1];
+    if (q->shape[0] != N || topk_idx->shape[0] != N) c.fail(MSA_ERR_SHAPE);
+    if (k_cache->shape[1] != kBlock || k_cache->shape[3] != D) c.fail(MSA_ERR_SHAPE);
+    for (int i = 0; i < 4; ++i)
+        if (v_cache->shape[i] != k_cache->shape[i]) c.fail(MSA_ERR_SHAPE);
+    if (out->shape[0] != N || out->shape[1] != Hq || out->shape[2] != D) c.fail(MSA_ERR_SHAPE);
+    if (Hkv < 1 || Hq < 1 || Hq % Hkv) c.fail(MSA_ERR_SHAPE);
+    if (K < 1) c.fail(MSA_ERR_SHAPE);
+    if (!c.ok()) { set_error(c.err); return; }
+    if (!attention_supported(etype(q->dtype), etype(k_cache->dtype), (int)D, (int)(Hq / Hkv)))
+        c.fail(MSA_ERR_UNSUPPORTED);
+    if (!fits_i32(N) || !fits_i32(P) || !fits_i32(K)) c.fail(MSA_ERR_UNSUPPORTED);
+    rows16(c, q);
+    rows16(c, k_cache);
+    rows16(c, v_cache);
+    if (!c.ok()) { set_error(c.err); return; }
+    if (N == 0) return;
+    const size_t need = attn_workspace_bytes((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv,
+                                             (int32_t)D, (int32_t)K);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) {
+        set_error(MSA_ERR_WORKSPACE);
+        return;
+    }
+
+    AttnParams p{};
+    p.q = q->data; p.q_sn = q->stride[0]; p.q_sh = q->stride[1];
+    p.k_cache = k_cache->data;
+    p.k_sp = k_cache->stride[0]; p.k_sb = k_cache->stride[1]; p.k_sh = k_cache->stride[2];
+    p.v_cache = v_cache->data;
+    p.v_sp = v_cache->stride[0]; p.v_sb = v_cache->stride[1]; p.v_sh = v_cache->stride[2];
+    p.bt = (const int32_t *)block_table->data;
+    p.bt_sr = block_table->stride[0]; p.bt_sj = block_table->stride[1];
+    p.seq_lens = (const int32_t *)seq_lens->data; p.sl_s = seq_lens->stride[0];
+    p.topk = (const int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
+    p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
+    p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
+    p.splits = attn_splits((int32_t)R, tokens_per_row, (int32_t)Hkv, (int32_t)K);
+    p.sm_scale = sm_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+    attn_carve_workspace(workspace, p.splits, (int32_t)N, (int32_t)Hq, (int32_t)D, &p.part_m,
+                         &p.part_l, &p.part_acc);
+    if (launch_attention(p, etype(q->dtype), etype(k_cache->dtype), (int)D, stream) != hipSuccess) {
+        set_error(MSA_ERR_LAUNCH);
+        return;
+    }
+    ReduceParams rp{};
+    rp.part_m = p.part_m; rp.part_l = p.part_l; rp.part_acc = p.part_acc;
+    rp.out = out->data; rp.o_sn = out->stride[0]; rp.o_sh = out->stride[1]; rp.o_sd = out->stride[2];
+    rp.N = (int32_t)N; rp.Hq = (int32_t)Hq; rp.D = (int32_t)D; rp.splits = p.splits;
+    rp.out_bf16 = out->dtype == MSA_BF16;
+    rp.v_scale = v_scale;
+    if (launch_reduce(rp, stream) != hipSuccess) set_error(MSA_ERR_LAUNCH);
+}
+
+}  // extern "C"

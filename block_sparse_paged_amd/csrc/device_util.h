@@ -1,0 +1,87 @@
+// Device helpers for gfx950 (CDNA4, wave64): FP8/bf16 conversions and
+// cross-lane reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace msa {
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Two OCP E4M3FN codes (byte pair 0-1 or 2-3 of `w`) -> two bf16.  Exact: every
+// E4M3FN value (normal, subnormal, NaN) is representable in bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+    bf16x2 r = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two E4M3FN codes -> two fp32 (exact).
+template <bool HI>
+__device__ __forceinline__ f32x2 fp8x2_to_f32x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Lane permutes through DPP (row = 16 lanes).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;       // lane i <-> 15-i within 16
+
+// Sum over aligned groups of W lanes (W power of two, <= 64); every lane of a
+// group ends with the group sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (W >= 2) v += dpp_f32<kDppXor1>(v);
+    if constexpr (W >= 4) v += dpp_f32<kDppXor2>(v);
+    if constexpr (W >= 8) v += dpp_f32<kDppHalfMirror>(v);
+    if constexpr (W >= 16) v += dpp_f32<kDppMirror>(v);
+    if constexpr (W >= 32) v += __shfl_xor(v, 16);
+    if constexpr (W >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+template <int W>
+__device__ __forceinline__ float group_max(float v) {
+    if constexpr (W >= 2) v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    if constexpr (W >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    if constexpr (W >= 8) v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    if constexpr (W >= 16) v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+    if constexpr (W >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+// Max over lanes whose index differs only in bits >= log2(FROM) (all lanes
+// holding equal values within groups of FROM).
+template <int FROM>
+__device__ __forceinline__ float max_across_groups(float v) {
+#pragma unroll
+    for (int off = FROM; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    return v;
+}
+
+}  // namespace msa

@@ -1,0 +1,176 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) MSA sparse-layer decode attention library.
+ *
+ * Three stages, one call each, in the write-into-output style of the Cacheon
+ * "Kernel ABI" page (section "Core rules"): the caller allocates every output
+ * (and poisons it), passes arguments in the order below together with the HIP
+ * stream to run on, and gets nothing back.  Each call
+ *   - writes every logical cell of its outputs, honouring the strides given;
+ *   - never writes an input;
+ *   - allocates nothing, keeps no pointer after it returns, synchronises
+ *     nothing on the host and only enqueues work on `stream`, so it may be
+ *     captured into a HIP graph and replayed with new input values at the
+ *     same addresses (Cacheon "Slot contract", section "CUDA graph contract");
+ *   - returns void.  When an argument is outside the supported domain the call
+ *     enqueues nothing (outputs keep their poison) and records an error code
+ *     that msa_get_last_error() returns.  A launch failure is recorded the
+ *     same way and never retried.
+ *
+ * Tensors are passed as msa_tensor descriptors: a device pointer to element
+ * [0,...,0], a dtype, and per-dimension sizes and strides counted in
+ * elements.  The library reads descriptors on the host only.
+ *
+ * Notation: R request rows, T query tokens per row, N = R*T query tokens
+ * (token n = r*T + t), B = 128 tokens per block/page, MB logical blocks per
+ * row (block_table width), P physical pages in the pool, Hq/Hkv query/KV
+ * heads, D head dim, Di index dim, k top-k width.
+ *
+ * Visibility (a reading: the pages leave it open): query token n = r*T + t
+ * sees key positions [0, V(n)) with V(n) = max(0, seq_lens[r] - (T-1-t)),
+ * i.e. the row's T new tokens are already in the cache and are causal among
+ * themselves (1 + 3 speculative tokens per row in the vLLM design note
+ * "MiniMax-M3 decode through the ATOM kernel library", "Supported
+ * experiment").  Logical block j of row r lives in physical page
+ * block_table[r][j].
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *hipStream_t;   /* same typedef as hip_runtime_api.h */
+
+typedef enum msa_dtype {
+    MSA_F32 = 0,
+    MSA_BF16 = 1,
+    MSA_FP8_E4M3FN = 2,   /* OCP E4M3FN codes, one byte each */
+    MSA_I32 = 3
+} msa_dtype;
+
+#define MSA_MAX_DIMS 4
+
+typedef struct msa_tensor {
+    void *data;                     /* device pointer to element [0,...,0]      */
+    int32_t dtype;                  /* msa_dtype                                */
+    int32_t ndim;
+    int64_t shape[MSA_MAX_DIMS];
+    int64_t stride[MSA_MAX_DIMS];   /* in elements; may be any value >= 0       */
+} msa_tensor;
+
+typedef enum msa_status {
+    MSA_OK = 0,
+    MSA_ERR_NULL = 1,          /* a required pointer is NULL                          */
+    MSA_ERR_DTYPE = 2,         /* dtype outside the supported set                     */
+    MSA_ERR_SHAPE = 3,         /* ndim or sizes disagree between arguments            */
+    MSA_ERR_LAYOUT = 4,        /* innermost stride / alignment the kernels need       */
+    MSA_ERR_UNSUPPORTED = 5,   /* block size, head dim, group size, k, ... not served */
+    MSA_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required          */
+    MSA_ERR_ARG = 7,           /* a scalar argument is out of range                   */
+    MSA_ERR_LAUNCH = 8         /* the HIP runtime refused a launch                    */
+} msa_status;
+
+/*
+ * Stage 1 -- block scores.  Cacheon "Kernel ABI", "Attention block slots",
+ * attention.msa_block_score (a per-query block-max score sheet) and
+ * attention.msa_prefill_block_score (the same sheet for prefill queries).  The
+ * pages leave the score open; this library computes
+ *     scores[n][j] = idx_scale * max_{s visible to n, s in block j}
+ *                    sum_d q_idx[n][d] * index_k[block_table[r][j]][s - j*B][d]
+ * and -inf when block j holds no key visible to token n.  FP8 codes are
+ * decoded exactly; products and sums are fp32.
+ *
+ *   q_idx       [N, Di]     bf16 | f32      innermost stride 1
+ *   index_k     [P, B, Di]  fp8e4m3fn | f32 innermost stride 1, rows 16-byte aligned
+ *   block_table [R, MB]     i32             any strides
+ *   seq_lens    [R]         i32             seq_lens[r] <= MB*B (larger is clamped)
+ *   tokens_per_row  T >= 1, N = R*T
+ *   block_size  must be 128
+ *   idx_scale   > 0, finite (static per-tensor dequantisation scale)
+ *   scores      [N, MB]     f32 OUT         any strides
+ * Di must be 32, 64 or 128.  A visible block whose physical page id lies
+ * outside [0, P) scores NaN (the page is not read).  Queries with T >= 16
+ * per row run on MFMA tiles; smaller T on vector ALUs.
+ */
+void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
+                     const msa_tensor *block_table, const msa_tensor *seq_lens,
+                     int32_t tokens_per_row, int32_t block_size, float idx_scale,
+                     msa_tensor *scores, hipStream_t stream);
+
+/*
+ * Stage 2 -- top-k block selection.  Cacheon "Kernel ABI", "Attention block
+ * slots" (attention.decode consumes nonnegative block ids, -1 = none;
+ * attention.msa_prefill_block_score: unused output cells are -1) and
+ * "Correctness is target-owned" (selections are graded as sets, so the order
+ * inside a row is free; this library emits ascending block ids).
+ * Per score row: candidates are the finite and +inf scores (-inf and NaN are
+ * not); the k largest are taken with ties broken toward the lower block id
+ * and -0 equal to +0; they are written in ascending block id and the row is
+ * padded with -1 when it has fewer than k candidates.  Deterministic.
+ *
+ *   scores   [N, MB]  f32  any strides, 1 <= MB <= 2048
+ *   k        1 <= k <= MB
+ *   topk_idx [N, k]   i32 OUT  any strides
+ */
+void msa_select_topk(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
+                     hipStream_t stream);
+
+/*
+ * Workspace bytes msa_sparse_decode needs for these sizes (split-K partials).
+ * Depends on the sizes only, not on the device or the data.
+ */
+size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
+                                         int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t k);
+
+/*
+ * Stage 3 -- sparse attention over the selected pages.  Cacheon "Kernel ABI",
+ * "Attention block slots", attention.decode: scaled-dot-product attention of
+ * each query over exactly the supplied nonnegative block ids, excluding -1
+ * entries and key positions at or beyond its visibility; query head h reads
+ * KV head h / (Hq/Hkv) (attention.sdpa).  With static scalar scales (vLLM
+ * design note, "Supported experiment"):
+ *     logit_s = sm_scale * k_scale * sum_d q[n][h][d] * k_code[s][d]
+ *     out[n][h] = v_scale * sum_s softmax(logit)_s * v_code[s]
+ * over the visible keys s of the selected blocks; 0 when there is none.
+ * Ids outside [0, MB) count as -1; a block whose page id lies outside [0, P)
+ * is skipped; duplicate ids in one row count once.
+ *
+ *   q           [N, Hq, D]      bf16 | f32      innermost stride 1
+ *   k_cache     [P, B, Hkv, D]  fp8e4m3fn | f32 innermost stride 1, 16-byte aligned rows
+ *   v_cache     [P, B, Hkv, D]  same dtype and shape as k_cache
+ *   block_table [R, MB] i32, seq_lens [R] i32   as for msa_block_score
+ *   topk_idx    [N, k]          i32             any strides; shared by all KV heads
+ *   tokens_per_row  T >= 1
+ *   out         [N, Hq, D]      bf16 | f32 OUT  any strides
+ *   sm_scale, k_scale, v_scale  finite floats
+ *   block_size  must be 128
+ *   workspace   device scratch of at least msa_sparse_decode_workspace_bytes(...)
+ *               bytes, 256-byte aligned; contents on entry are irrelevant
+ * D must be 64 or 128.  When Hq/Hkv == 16 with bf16 queries and FP8 caches the
+ * QK^T and PV products run on bf16 MFMA tiles (FP8 decoded exactly, P rounded
+ * to bf16); otherwise on vector ALUs in fp32.
+ */
+void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
+                       const msa_tensor *v_cache, const msa_tensor *block_table,
+                       const msa_tensor *seq_lens, const msa_tensor *topk_idx,
+                       int32_t tokens_per_row, msa_tensor *out,
+                       float sm_scale, float k_scale, float v_scale, int32_t block_size,
+                       void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Error code recorded by the most recent failing call on this thread, then
+ * reset to MSA_OK.  Returns MSA_OK when no call failed since the last read. */
+int32_t msa_get_last_error(void);
+
+/* Static description of an msa_status code (never NULL). */
+const char *msa_error_string(int32_t code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

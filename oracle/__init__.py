@@ -207,8 +207,8 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
     Goes through float32 first only when that step is exact for the comparison
     at hand; to avoid double rounding it rounds from float64 directly here.
     """
-    x = np.asarray(x, dtype=np.float64)
-    out = np.empty_like(x)
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, dtype=np.float64)
     flat = x.reshape(-1)
     res = out.reshape(-1)
     m, e = np.frexp(flat)                     # flat = m * 2^e, 0.5 <= |m| < 1

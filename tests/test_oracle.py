@@ -386,3 +386,5 @@ def test_round_bf16_matches_torch(orc):
     x32 = x.astype(np.float32).astype(np.float64)      # exactly representable in f32
     ref = torch.from_numpy(x32).to(torch.float32).to(torch.bfloat16).double().numpy()
     assert np.array_equal(orc.round_bf16(x32), ref)
+    m = x32[:6000].reshape(60, 100)
+    assert np.array_equal(orc.round_bf16(m.T), ref[:6000].reshape(60, 100).T)   # strided input

@@ -1,0 +1,219 @@
+"""GPU parity: the HIP library against the CPU oracle on seeded workloads.
+
+Covers the five workload families at full size (tiny fp32; 4-row decode
+bucket at 16K; the 1/4/8/16-row bucket sweep with ragged lengths and padded
+rows; the 4 x 2048-token prefill score -> select; the 16-row 16K HBM-bound
+decode with k in {8, 16, 32, 128}) plus small cases that exercise ragged
+tails, token groups, head dims, index dims, shared pages and the vector-ALU
+paths.  The 16-row config runs in the same launch configuration as the bench.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from msa_harness import (check_attention, check_scores, check_topk_end_to_end,
+                         check_topk_isolated, full_step_parity, oracle_attention, oracle_scores,
+                         run_attend, run_score, run_select, upload)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def msa():
+    import block_sparse_paged_amd as m
+    return m
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def test_tiny_fp32(msa):
+    c = synth.tiny()
+    _say(f"case {c.name}")
+    res = full_step_parity(msa, c)
+    _say(str(res))
+
+
+def test_decode_bucket4(msa):
+    c = synth.decode_bucket4()
+    _say(f"case {c.name}")
+    _say(str(full_step_parity(msa, c)))
+
+
+@pytest.mark.parametrize("R", [1, 4, 8, 16])
+def test_bucket_sweep(msa, R):
+    c = synth.bucket_sweep(R)
+    _say(f"case {c.name} lens={c.seq_lens.tolist()}")
+    _say(str(full_step_parity(msa, c)))
+
+
+def test_bucket_sweep_padded_rows(msa):
+    c = synth.bucket_sweep(8, seed=3100, pad_rows=(2, 7))
+    _say(f"case {c.name}+pad lens={c.seq_lens.tolist()}")
+    d = upload(c)
+    scores = run_score(msa, c, d)
+    topk = run_select(msa, c, scores)
+    out = run_attend(msa, c, d, topk)
+    torch.cuda.synchronize()
+    gs, gt, go = scores.cpu().numpy(), topk.cpu().numpy(), out.float().cpu().numpy()
+    for r in (2, 7):
+        rows = slice(r * c.T, (r + 1) * c.T)
+        assert np.isneginf(gs[rows]).all()
+        assert (gt[rows] == -1).all()
+        assert (go[rows] == 0).all()
+    ref = oracle_scores(c)
+    check_scores(gs, ref)
+    check_topk_isolated(gt, gs)
+    check_topk_end_to_end(gt, ref)
+    check_attention(out, oracle_attention(c, gt))
+
+
+def test_prefill_score_select(msa):
+    c = synth.prefill()
+    _say(f"case {c.name}")
+    d = upload(c)
+    scores = run_score(msa, c, d)
+    topk = run_select(msa, c, scores)
+    torch.cuda.synchronize()
+    gs, gt = scores.cpu().numpy(), topk.cpu().numpy()
+    assert gt.shape == (8192, 16)
+    check_topk_isolated(gt, gs)              # whole sheet, bit-exact
+    # sampled rows of the oracle: the first and last tokens of every request and
+    # a stretch across a block boundary in the middle
+    rows = []
+    for r in range(c.R):
+        base = r * c.T
+        rows += list(range(base, base + 48)) + list(range(base + 1000, base + 1040))
+        rows += list(range(base + c.T - 48, base + c.T))
+    ref = np.full_like(gs, np.nan, dtype=np.float64)
+    spans = []
+    rows = sorted(set(rows))
+    start = prev = rows[0]
+    for x in rows[1:]:
+        if x != prev + 1:
+            spans.append((start, prev + 1))
+            start = x
+        prev = x
+    spans.append((start, prev + 1))
+    for a, b in spans:
+        ref[a:b] = oracle_scores(c, n_range=(a, b), threads=16)[a:b]
+    check_scores(gs, ref, rows=rows)
+    check_topk_end_to_end(gt, np.where(np.isnan(ref), -np.inf, ref), rows=rows)
+
+
+@pytest.mark.parametrize("k", [8, 16, 32, 128])
+def test_hbm_decode(msa, k):
+    c = synth.hbm_decode(k)
+    _say(f"case {c.name}")
+    _say(str(full_step_parity(msa, c, threads=16)))
+
+
+def test_hbm_decode_all_blocks_is_dense(msa):
+    import oracle
+    c = synth.hbm_decode(128)
+    _say(f"case {c.name} dense")
+    d = upload(c)
+    topk = torch.arange(128, dtype=torch.int32, device="cuda").repeat(c.N, 1)
+    out = run_attend(msa, c, d, topk)
+    torch.cuda.synchronize()
+    rows = list(range(0, c.N, 7))
+    dense = np.full((c.N, c.Hq, c.D), np.nan)
+    for n in rows:
+        dense[n:n + 1] = oracle.dense_attention(c.q, c.k_cache, c.v_cache, c.block_table,
+                                                c.seq_lens, c.T, c.sm_scale, c.k_scale,
+                                                c.v_scale, n_range=(n, n + 1))[n:n + 1]
+    check_attention(out, dense, rows=rows)
+
+
+SMALL = [
+    dict(R=2, T=4, lens=(700, 1500), k=4),
+    dict(R=3, T=1, lens=(129, 5000, 1), k=8),
+    dict(R=2, T=5, lens=(1000, 2100), k=6),          # two token groups per row
+    dict(R=1, T=8, lens=(3000,), k=3),
+    dict(R=2, T=4, lens=(700, 1500), k=4, D=64, Di=64),
+    dict(R=2, T=4, lens=(900, 300), k=4, Di=32),
+    dict(R=2, T=2, lens=(2000, 2500), k=5, shared_pages=True, P=40),
+    dict(R=2, T=40, lens=(300, 1700), k=4),          # MFMA score path, ragged
+    dict(R=1, T=130, lens=(1200,), k=3, D=64, Di=64),
+    dict(R=2, T=4, lens=(600, 900), k=4, Hq=32),     # 2 KV heads via Hkv below
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=[str(i) for i in range(len(SMALL))])
+def test_small_fp8(msa, spec):
+    spec = dict(spec)
+    lens = spec.pop("lens")
+    hq = spec.pop("Hq", 16)
+    if hq == 32:
+        c = synth.make_case("small_hkv2", R=spec["R"], T=spec["T"], Hq=32, Hkv=2, D=128,
+                            Di=128, seq_lens=list(lens), P=30, k=spec["k"], seed=21)
+    else:
+        c = synth.small_fp8(lens=lens, **spec)
+    _say(f"case {c.name} {spec} lens={lens}")
+    _say(str(full_step_parity(msa, c)))
+
+
+FP32 = [
+    dict(R=2, T=3, Hq=4, Hkv=1, D=64, Di=32, lens=(500, 300), k=2),
+    dict(R=1, T=4, Hq=16, Hkv=1, D=128, Di=128, lens=(1000,), k=3),
+    dict(R=2, T=2, Hq=8, Hkv=2, D=64, Di=64, lens=(260, 900), k=4),
+]
+
+
+@pytest.mark.parametrize("spec", FP32, ids=[str(i) for i in range(len(FP32))])
+def test_small_fp32(msa, spec):
+    spec = dict(spec)
+    lens = spec.pop("lens")
+    nblk = sum((x + 127) // 128 for x in lens)
+    c = synth.make_case("small_fp32", seq_lens=list(lens), P=nblk + 3, fp8=False, seed=31, **spec)
+    _say(f"case {c.name} {spec}")
+    _say(str(full_step_parity(msa, c)))
+
+
+def test_mixed_precision_variants(msa):
+    """bf16 queries with fp32 caches, fp32 queries with FP8 caches, fp32 output."""
+    base = synth.small_fp8(R=2, T=4, lens=(700, 1300), k=4, seed=41)
+    variants = {
+        "f32q_fp8kv": dict(q=base.q.float(), q_idx=base.q_idx.float()),
+        "bf16q_f32kv": dict(index_k=base.index_k.view(torch.float8_e4m3fn).float(),
+                            k_cache=base.k_cache.view(torch.float8_e4m3fn).float(),
+                            v_cache=base.v_cache.view(torch.float8_e4m3fn).float()),
+    }
+    for name, repl in variants.items():
+        c = synth.Case(**{**base.__dict__, **repl})
+        c.name = name
+        _say(f"case {name}")
+        _say(str(full_step_parity(msa, c)))
+    c = base
+    d = upload(c)
+    scores = run_score(msa, c, d)
+    topk = run_select(msa, c, scores)
+    out = run_attend(msa, c, d, topk, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_attention(out, oracle_attention(c, topk.cpu().numpy()))
+
+
+def test_caller_topk_with_gaps(msa):
+    """attention on a caller-made selection: -1 holes, out-of-range ids,
+    duplicates, blocks past the visible range, and empty rows."""
+    c = synth.small_fp8(R=2, T=4, lens=(1000, 600), k=6, seed=51)
+    d = upload(c)
+    tk = synth.random_topk(c, seed=52).numpy()
+    tk[0, 1] = -1
+    tk[1, 2] = c.MB + 3
+    tk[2, 0] = tk[2, 3]                            # duplicate counts once
+    tk[4, 5] = 7                                   # past row 1's visible blocks (0..4)
+    tk[5, :] = -1                                  # empty selection
+    out = run_attend(msa, c, d, torch.from_numpy(tk).cuda())
+    torch.cuda.synchronize()
+    clean = tk.copy()
+    clean[clean >= c.MB] = -1
+    clean[2, 0] = -1
+    ref = oracle_attention(c, clean)
+    check_attention(out, ref)
+    assert (out[5].float().cpu() == 0).all()
