@@ -125,7 +125,7 @@ def main():
     out = [torch.full((case.N, case.Hq, case.D), float("nan"), dtype=torch.bfloat16, device=dev)
            for _ in range(M)]
     wsb = msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, case.k)
-    ws = [torch.empty(wsb, dtype=torch.uint8, device=dev) for _ in range(M)]
+    ws = [torch.zeros(wsb, dtype=torch.uint8, device=dev) for _ in range(M)]
 
     def call(name, i):
         idx, kc, vc = pools[i]

@@ -220,7 +220,7 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
     if (!c.ok()) { set_error(c.err); return; }
     if (!attention_supported(etype(q->dtype), etype(k_cache->dtype), (int)D, (int)(Hq / Hkv)))
         c.fail(MSA_ERR_UNSUPPORTED);
-    if (!fits_i32(N) || !fits_i32(P) || !fits_i32(K)) c.fail(MSA_ERR_UNSUPPORTED);
+    if (!fits_i32(N) || !fits_i32(P) || K > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
     rows16(c, q);
     rows16(c, k_cache);
     rows16(c, v_cache);
@@ -245,14 +245,20 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
     p.topk = (const int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
     p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
     p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
-    p.splits = attn_splits((int32_t)R, tokens_per_row, (int32_t)Hkv, (int32_t)K);
+    const int qt = etype(q->dtype), kt = etype(k_cache->dtype);
+    const AttnPlan plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kt);
+    p.splits = plan.splits;
+    p.bpw = plan.bpw;
     p.sm_scale = sm_scale; p.k_scale = k_scale; p.v_scale = v_scale;
-    attn_carve_workspace(workspace, p.splits, (int32_t)N, (int32_t)Hq, (int32_t)D, &p.part_m,
-                         &p.part_l, &p.part_acc);
-    if (launch_attention(p, etype(q->dtype), etype(k_cache->dtype), (int)D, stream) != hipSuccess) {
+    attn_carve_workspace(workspace, p.splits, (int32_t)N, (int32_t)Hq, (int32_t)Hkv, (int32_t)D,
+                         &p.part_m, &p.part_l, &p.part_acc, &p.counters);
+    p.out = out->data; p.o_sn = out->stride[0]; p.o_sh = out->stride[1]; p.o_sd = out->stride[2];
+    p.out_bf16 = out->dtype == MSA_BF16;
+    if (launch_attention(p, qt, kt, (int)D, stream) != hipSuccess) {
         set_error(MSA_ERR_LAUNCH);
         return;
     }
+    if (plan.mfma) return;                       // the MFMA path merges its splits itself
     ReduceParams rp{};
     rp.part_m = p.part_m; rp.part_l = p.part_l; rp.part_acc = p.part_acc;
     rp.out = out->data; rp.o_sn = out->stride[0]; rp.o_sh = out->stride[1]; rp.o_sd = out->stride[2];

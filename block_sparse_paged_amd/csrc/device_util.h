@@ -41,6 +41,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
 }
 
+// Two fp32 -> packed bf16 with the hardware converter (v_cvt_pk_bf16_f32,
+// round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 2^x on the transcendental unit, no denormal fix-up (for x <= 0 whose result
+// only feeds softmax weights; -inf gives 0).
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Lane permutes through DPP (row = 16 lanes).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {

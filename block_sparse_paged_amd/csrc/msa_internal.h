@@ -38,9 +38,13 @@ struct AttnParams {
     const int32_t *topk; int64_t tk_sn, tk_si;     // [N, k]
     int32_t R, T, MB, P, Hq, Hkv, k;
     int32_t splits;                                // S
+    int32_t bpw;                                   // selected pages per wave (token path)
     float sm_scale, k_scale, v_scale;
     // split-K partials (workspace): m, l [S, N, Hq]; acc [S, N, Hq, D]
     float *part_m, *part_l, *part_acc;
+    int32_t *counters;                             // [N, Hkv], zero between calls
+    void *out; int64_t o_sn, o_sh, o_sd;           // [N, Hq, D] (token path writes it)
+    int32_t out_bf16;
 };
 
 struct ReduceParams {
@@ -51,10 +55,16 @@ struct ReduceParams {
     float v_scale;
 };
 
-int attn_splits(int32_t R, int32_t T, int32_t Hkv, int32_t k);
+// Split plan of msa_sparse_decode for the given sizes and element types.
+struct AttnPlan {
+    bool mfma;          // per-token MFMA kernel with in-kernel merge (else union VALU + reduce)
+    int32_t splits;
+    int32_t bpw;
+};
+AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type);
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k);
-void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t D,
-                          float **m, float **l, float **acc);
+void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                          float **m, float **l, float **acc, int32_t **counters);
 
 // Launchers return hipSuccess or the launch error; dispatch on element types.
 hipError_t launch_score(const ScoreParams &p, int q_type, int k_type, int Di, hipStream_t s);
@@ -64,5 +74,6 @@ hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
 
 bool score_supported(int q_type, int k_type, int Di);
 bool attention_supported(int q_type, int kv_type, int D, int G);
+bool attention_uses_mfma(int q_type, int kv_type, int G);
 
 }  // namespace msa

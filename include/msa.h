@@ -120,8 +120,9 @@ void msa_select_topk(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
                      hipStream_t stream);
 
 /*
- * Workspace bytes msa_sparse_decode needs for these sizes (split-K partials).
- * Depends on the sizes only, not on the device or the data.
+ * Workspace bytes msa_sparse_decode needs for these sizes: split partials plus
+ * one arrival counter per (query token, KV head).  Depends on the sizes only,
+ * not on the device, the element types or the data.
  */
 size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
                                          int32_t num_q_heads, int32_t num_kv_heads,
@@ -150,7 +151,11 @@ size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
  *   sm_scale, k_scale, v_scale  finite floats
  *   block_size  must be 128
  *   workspace   device scratch of at least msa_sparse_decode_workspace_bytes(...)
- *               bytes, 256-byte aligned; contents on entry are irrelevant
+ *               bytes, 256-byte aligned, owned by the caller.  Zero-fill it once
+ *               before its first use; every call leaves its counters at zero
+ *               again, so the same workspace can be reused (and replayed in a
+ *               graph) without clearing.  Calls that share one workspace must
+ *               not run concurrently.
  * D must be 64 or 128.  When Hq/Hkv == 16 with bf16 queries and FP8 caches the
  * QK^T and PV products run on bf16 MFMA tiles (FP8 decoded exactly, P rounded
  * to bf16); otherwise on vector ALUs in fp32.

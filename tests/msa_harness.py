@@ -79,7 +79,7 @@ def run_select(msa, case, scores, topk: Optional[torch.Tensor] = None, k: Option
 
 def workspace(msa, case, k: int) -> torch.Tensor:
     nbytes = msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, k)
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    return torch.zeros(max(nbytes, 1), dtype=torch.uint8, device="cuda")
 
 
 def run_attend(msa, case, d: Dev, topk, out: Optional[torch.Tensor] = None,

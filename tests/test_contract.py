@@ -175,3 +175,18 @@ def test_rejected_call_leaves_poison(msa):
                               out, c.sm_scale, c.k_scale, c.v_scale, c.B, small_ws)
     torch.cuda.synchronize()
     assert torch.isnan(scores).all() and torch.isnan(out.float()).all()
+
+
+def test_workspace_counters_left_zero(msa):
+    """The split-merge arrival counters (the first N*Hkv int32 of the workspace)
+    are zero again after every call, so a workspace can be reused without clearing."""
+    for k in (16, 5, 128):
+        c = synth.small_fp8(R=2, T=4, lens=(3000, 16384), k=min(k, 24), seed=95, P=200)
+        d = upload(c)
+        tk = synth.random_topk(c, seed=96).cuda()
+        ws = workspace(msa, c, tk.shape[1])
+        for _ in range(3):
+            run_attend(msa, c, d, tk, ws=ws)
+        torch.cuda.synchronize()
+        ctr = ws[: c.N * c.Hkv * 4].view(torch.int32)
+        assert (ctr == 0).all()
