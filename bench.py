@@ -2,19 +2,22 @@
 
 A step is one pass of the whole hot path over one batch: block scores over the
 FP8 index cache, top-k block selection, and sparse attention over the selected
-FP8 K/V pages with its split-K merge -- the three C-ABI calls back to back on
-one stream.  Workload: 16 request rows x 4 query tokens (1 + 3 speculative),
-16384-token context per row (128 blocks of 128), 16 query heads / 1 KV head,
-head dim 128, index dim 128, top-k 16, a 4096-page pool with random
-non-overlapping block tables (synthetic seeded data).
+FP8 K/V pages with its split-K merge.  The timed step is msa_decode_step: the
+score launch, then msa_select_sparse_decode's attention launch, which selects
+each token's blocks itself, and the split merge.  Each public call on its own
+and the step as the three separate calls are timed too.
+Workload: 16 request rows x 4 query tokens (1 + 3 speculative), 16384-token
+context per row (128 blocks of 128), 16 query heads / 1 KV head, head dim 128,
+index dim 128, top-k 16, a 4096-page pool with random non-overlapping block
+tables (synthetic seeded data).
 
 Timing: M independent copies of the pools (192 MiB each) are rotated so that
 each step reads cold data rather than the 256 MB Infinity Cache; M steps are
 captured into one HIP graph, replayed after warm-up, and bracketed by HIP
-events after a device synchronisation.  The per-kernel durations used for the
-roofline come from graphs of M back-to-back launches of each call, timed the
-same way on the same stream.  The CPU baseline is the oracle (plain C, fp64)
-running one full step of the same batch on the host cores.
+events on the stream the kernels run on.  The roofline figure is for the
+attention launch of the step (msa_select_sparse_decode timed on its own the
+same way): its algorithmic bytes over its duration.  The CPU baseline is the
+oracle (plain C, fp64) running full steps of the same batch on the host cores.
 
 Prints one JSON line.
 """
@@ -33,6 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# the launches msa_select_sparse_decode makes at this shape
+ROOFLINE_KERNEL = "attn_token_select_kernel<128,false> + attn_reduce_kernel"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -44,8 +49,8 @@ def parse():
     ap.add_argument("--k", type=int, default=16)
     ap.add_argument("--copies", type=int, default=8, help="pool copies rotated per graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernels", default="score,select,decode",
-                    help="per-call timing graphs to build")
+    ap.add_argument("--kernels", default="score,select,decode,select_decode,calls",
+                    help="extra timing graphs to build (per call, and the three-call step)")
     return ap.parse_args()
 
 
@@ -59,7 +64,8 @@ def kernel_source_digest() -> str:
 
 
 def algorithmic_bytes(case, topk: np.ndarray) -> dict:
-    """Bytes each call must move at minimum (each touched page once per row)."""
+    """Bytes each call must move at minimum: every page a row touches once per
+    row, each small input once, each output once."""
     R, T, N, MB, B = case.R, case.T, case.N, case.MB, case.B
     lens = case.seq_lens.numpy().astype(np.int64)
     Di, D, Hq, Hkv, k = case.Di, case.D, case.Hq, case.Hkv, topk.shape[1]
@@ -70,31 +76,38 @@ def algorithmic_bytes(case, topk: np.ndarray) -> dict:
         ids = ids[ids >= 0]
         kv_tokens += int(sum(min(B, lens[r] - j * B) for j in ids if j * B < lens[r]))
     kv = kv_tokens * Hkv * D * 1 * 2
-    small_bt = R * MB * 4 + R * 4
-    score = index + N * Di * 2 + N * MB * 4 + small_bt
-    select = N * MB * 4 + N * k * 4
-    attend = kv + N * Hq * D * 2 + N * k * 4 + small_bt
-    reduce_ = N * Hq * D * 2
-    return dict(score=score, select=select, attend=attend, reduce=reduce_,
-                decode=attend + reduce_, step=score + select + attend + reduce_,
-                index=index, kv=kv)
+    paging = R * MB * 4 + R * 4                 # block table + seq_lens
+    score_sheet = N * MB * 4
+    sel = N * k * 4
+    qo = N * Hq * D * 2 * 2                     # bf16 queries in, bf16 output out
+    score = index + N * Di * 2 + score_sheet + paging
+    select = score_sheet + sel
+    attend = kv + qo + sel + paging
+    select_decode = kv + qo + score_sheet + sel + paging
+    return dict(score=score, select=select, decode=attend, select_decode=select_decode,
+                step=score + select_decode, calls=score + select + attend, index=index, kv=kv)
 
 
-def cpu_baseline(case) -> dict:
+def cpu_baseline(case, min_wall: float = 1.0) -> dict:
+    """The oracle's full step on the host cores, repeated for at least min_wall s."""
     import oracle
     try:
-        threads = len(os.sched_getaffinity(0))
+        threads = min(16, len(os.sched_getaffinity(0)))
     except AttributeError:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    t0 = time.perf_counter()
-    s = oracle.block_score(case.q_idx, case.index_k, case.block_table, case.seq_lens, case.T,
-                           case.idx_scale, threads=threads)
-    tk = oracle.select_topk(s, case.k)
-    oracle.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens, tk,
-                         case.T, case.sm_scale, case.k_scale, case.v_scale, threads=threads)
-    dt = time.perf_counter() - t0
-    return {"value": round(1.0 / dt, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
-            "sample": f"one full step of the same {case.R}x{case.T}-token batch "
+        threads = min(16, os.cpu_count() or 1)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        s = oracle.block_score(case.q_idx, case.index_k, case.block_table, case.seq_lens, case.T,
+                               case.idx_scale, threads=threads)
+        tk = oracle.select_topk(s, case.k)
+        oracle.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                             tk, case.T, case.sm_scale, case.k_scale, case.v_scale, threads=threads)
+        steps += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_wall:
+            break
+    return {"value": round(steps / dt, 4), "unit": "steps/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} full steps of the same {case.R}x{case.T}-token batch "
                       f"(score+select+attend, fp64 C, {threads} threads), {dt:.2f} s wall"}
 
 
@@ -124,15 +137,23 @@ def main():
     topk = [torch.full((case.N, case.k), -1, dtype=torch.int32, device=dev) for _ in range(M)]
     out = [torch.full((case.N, case.Hq, case.D), float("nan"), dtype=torch.bfloat16, device=dev)
            for _ in range(M)]
-    wsb = msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, case.k)
-    ws = [torch.zeros(wsb, dtype=torch.uint8, device=dev) for _ in range(M)]
+    wsb = msa.msa_decode_step_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, case.k)
+    ws = [torch.zeros(wsb, dtype=torch.uint8, device=dev) for _ in range(M)]   # zero-filled once
 
     def call(name, i):
         idx, kc, vc = pools[i]
-        if name == "score":
+        if name == "step":
+            msa.msa_decode_step(q_idx, idx, q, kc, vc, bt, sl, case.T, case.k, case.B,
+                                case.idx_scale, case.sm_scale, case.k_scale, case.v_scale,
+                                scores[i], topk[i], out[i], ws[i])
+        elif name == "score":
             msa.msa_block_score(q_idx, idx, bt, sl, case.T, case.B, case.idx_scale, scores[i])
         elif name == "select":
             msa.msa_select_topk(scores[i], case.k, topk[i])
+        elif name == "select_decode":
+            msa.msa_select_sparse_decode(scores[i], case.k, topk[i], q, kc, vc, bt, sl, case.T,
+                                         out[i], case.sm_scale, case.k_scale, case.v_scale,
+                                         case.B, ws[i])
         else:
             msa.msa_sparse_decode(q, kc, vc, bt, sl, topk[i], case.T, out[i], case.sm_scale,
                                   case.k_scale, case.v_scale, case.B, ws[i])
@@ -153,7 +174,7 @@ def main():
                     call(name, i)
         return g
 
-    step_graph = capture(("score", "select", "decode"))
+    step_graph = capture(("step",))
     reps_w = max(1, a.warmup // M)
     reps = max(1, a.steps // M)
     steps = reps * M
@@ -176,8 +197,11 @@ def main():
     t_step = timed(step_graph, reps) / steps
 
     per_call = {}
-    for name in [n for n in a.kernels.split(",") if n]:
-        g = capture((name,))
+    names = [n for n in a.kernels.split(",") if n]
+    if "select_decode" not in names:          # the roofline launch is always timed
+        names.append("select_decode")
+    for name in names:
+        g = capture(("score", "select", "decode") if name == "calls" else (name,))
         with torch.cuda.stream(stream):
             for _ in range(max(1, reps_w // 4)):
                 g.replay()
@@ -187,10 +211,10 @@ def main():
     tk_host = topk[0].cpu().numpy()
     ab = algorithmic_bytes(case, tk_host)
     eff_gbs = ab["step"] / t_step / 1e9
-    # dominant call: the one with the longest launch duration
-    dom = max(per_call, key=per_call.get) if per_call else "decode"
-    dom_bytes = ab[dom]
-    dom_gbs = dom_bytes / per_call.get(dom, t_step) / 1e9
+    # dominant launch: the step's attention launch, timed on its own
+    dom = "select_decode"
+    t_dom = per_call.get(dom)
+    dom_gbs = ab[dom] / t_dom / 1e9 if t_dom else None
     traffic = None
     tfile = os.path.join(ROOT, "profiles", "traffic.json")
     if os.path.exists(tfile):
@@ -222,10 +246,11 @@ def main():
         "pct_of_hbm_peak": round(100.0 * eff_gbs / HBM_PEAK_GBS, 2),
         "algorithmic_bytes_per_step": ab["step"],
         "per_call_us": {k: round(v * 1e6, 3) for k, v in per_call.items()},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+        "roofline": {"bound": "hbm", "kernel": ROOFLINE_KERNEL, "achieved": round(dom_gbs, 1) if dom_gbs else None,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "algorithmic_bytes": dom_bytes},
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4) if dom_gbs else None, "traffic": traffic,
+                     "algorithmic_bytes": ab[dom],
+                     "duration_us": round(t_dom * 1e6, 3) if t_dom else None},
     }
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case)

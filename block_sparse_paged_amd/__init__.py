@@ -12,6 +12,12 @@ There is no CPU fallback: importing fails when the library is missing.
     msa_sparse_decode(q, k_cache, v_cache, block_table, seq_lens, topk_idx,
                       tokens_per_row, out, sm_scale, k_scale, v_scale,
                       block_size, workspace)
+    msa_select_sparse_decode(scores, k, topk_idx, q, k_cache, v_cache, block_table,
+                             seq_lens, tokens_per_row, out, sm_scale, k_scale, v_scale,
+                             block_size, workspace)
+    msa_decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
+                    tokens_per_row, k, block_size, idx_scale, sm_scale, k_scale,
+                    v_scale, scores, topk_idx, out, workspace)
 
 Each call writes into the outputs given (same argument order as the C ABI)
 and returns None; a rejected call raises MsaError and leaves the outputs as
@@ -37,7 +43,9 @@ _DTYPES = {
     torch.int32: MSA_I32,
 }
 EXPORTS = ("msa_block_score", "msa_select_topk", "msa_sparse_decode_workspace_bytes",
-           "msa_sparse_decode", "msa_get_last_error", "msa_error_string")
+           "msa_sparse_decode", "msa_select_sparse_decode", "msa_decode_step_workspace_bytes",
+           "msa_decode_step",
+           "msa_get_last_error", "msa_error_string")
 
 
 class msa_tensor(ctypes.Structure):
@@ -54,7 +62,7 @@ class MsaError(RuntimeError):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing; build it with "
-                          "`python -m block_sparse_paged_amd.build` (hipcc, gfx950)")
+                          "`python block_sparse_paged_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER(msa_tensor)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
@@ -66,6 +74,14 @@ def _load() -> ctypes.CDLL:
     lib.msa_sparse_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.msa_sparse_decode.restype = None
     lib.msa_sparse_decode.argtypes = [P, P, P, P, P, P, i32, P, f32, f32, f32, i32, vp, sz, vp]
+    lib.msa_select_sparse_decode.restype = None
+    lib.msa_select_sparse_decode.argtypes = [P, i32, P, P, P, P, P, P, i32, P, f32, f32, f32, i32,
+                                             vp, sz, vp]
+    lib.msa_decode_step_workspace_bytes.restype = sz
+    lib.msa_decode_step_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.msa_decode_step.restype = None
+    lib.msa_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, f32, f32, f32, f32, P, P, P,
+                                    vp, sz, vp]
     lib.msa_get_last_error.restype = i32
     lib.msa_get_last_error.argtypes = []
     lib.msa_error_string.restype = ctypes.c_char_p
@@ -134,4 +150,38 @@ def msa_sparse_decode(q, k_cache, v_cache, block_table, seq_lens, topk_idx,
     lib.msa_sparse_decode(*(ctypes.byref(x) for x in d[:6]), int(tokens_per_row),
                           ctypes.byref(d[6]), float(sm_scale), float(k_scale), float(v_scale),
                           int(block_size), ws_ptr, ws_bytes, _stream(stream))
+    _check()
+
+
+def msa_select_sparse_decode(scores, k: int, topk_idx, q, k_cache, v_cache, block_table,
+                             seq_lens, tokens_per_row: int, out, sm_scale: float, k_scale: float,
+                             v_scale: float, block_size: int, workspace, stream=None) -> None:
+    d = [tensor_desc(t) for t in (scores, topk_idx, q, k_cache, v_cache, block_table, seq_lens, out)]
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib.msa_select_sparse_decode(ctypes.byref(d[0]), int(k), *(ctypes.byref(x) for x in d[1:7]),
+                                 int(tokens_per_row), ctypes.byref(d[7]), float(sm_scale),
+                                 float(k_scale), float(v_scale), int(block_size), ws_ptr, ws_bytes,
+                                 _stream(stream))
+    _check()
+
+
+def msa_decode_step_workspace_bytes(rows: int, tokens_per_row: int, num_q_heads: int,
+                                    num_kv_heads: int, head_dim: int, k: int) -> int:
+    return int(lib.msa_decode_step_workspace_bytes(rows, tokens_per_row, num_q_heads,
+                                                   num_kv_heads, head_dim, k))
+
+
+def msa_decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
+                    tokens_per_row: int, k: int, block_size: int, idx_scale: float,
+                    sm_scale: float, k_scale: float, v_scale: float, scores, topk_idx, out,
+                    workspace, stream=None) -> None:
+    d = [tensor_desc(t) for t in (q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
+                                  scores, topk_idx, out)]
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib.msa_decode_step(*(ctypes.byref(x) for x in d[:7]), int(tokens_per_row), int(k),
+                        int(block_size), float(idx_scale), float(sm_scale), float(k_scale),
+                        float(v_scale), *(ctypes.byref(x) for x in d[7:]), ws_ptr, ws_bytes,
+                        _stream(stream))
     _check()

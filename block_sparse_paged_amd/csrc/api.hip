@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
+
 #include "msa.h"
 #include "msa_internal.h"
 
@@ -111,10 +113,15 @@ const char *msa_error_string(int32_t code) {
     return "unknown error";
 }
 
-void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
-                     const msa_tensor *block_table, const msa_tensor *seq_lens,
-                     int32_t tokens_per_row, int32_t block_size, float idx_scale,
-                     msa_tensor *scores, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// ---- validation + parameter building shared by the entry points ------------
+
+int32_t prep_score(const msa_tensor *q_idx, const msa_tensor *index_k, const msa_tensor *block_table,
+                   const msa_tensor *seq_lens, int32_t tokens_per_row, int32_t block_size,
+                   float idx_scale, msa_tensor *scores, ScoreParams &p, int &qt, int &kt, int &Di) {
     Check c;
     desc(c, q_idx, 2);
     desc(c, index_k, 3);
@@ -123,23 +130,23 @@ void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
     dtype_in(c, q_idx, {MSA_BF16, MSA_F32});
     dtype_in(c, index_k, {MSA_FP8_E4M3FN, MSA_F32});
     dtype_in(c, scores, {MSA_F32});
-    if (!c.ok()) { set_error(c.err); return; }
+    if (!c.ok()) return c.err;
     if (block_size != kBlock) c.fail(MSA_ERR_UNSUPPORTED);
     if (tokens_per_row < 1) c.fail(MSA_ERR_ARG);
     if (!(idx_scale > 0.f) || !isfinite(idx_scale)) c.fail(MSA_ERR_ARG);
     const int64_t R = block_table->shape[0], MB = block_table->shape[1];
     const int64_t N = R * (int64_t)tokens_per_row;
-    const int64_t Di = q_idx->shape[1];
+    Di = (int)q_idx->shape[1];
     if (q_idx->shape[0] != N || scores->shape[0] != N || scores->shape[1] != MB) c.fail(MSA_ERR_SHAPE);
     if (index_k->shape[1] != kBlock || index_k->shape[2] != Di) c.fail(MSA_ERR_SHAPE);
-    if (!score_supported(etype(q_idx->dtype), etype(index_k->dtype), (int)Di)) c.fail(MSA_ERR_UNSUPPORTED);
+    qt = etype(q_idx->dtype);
+    kt = etype(index_k->dtype);
+    if (!score_supported(qt, kt, Di)) c.fail(MSA_ERR_UNSUPPORTED);
     if (!fits_i32(N) || !fits_i32(index_k->shape[0])) c.fail(MSA_ERR_UNSUPPORTED);
     rows16(c, q_idx);
     rows16(c, index_k);
-    if (!c.ok()) { set_error(c.err); return; }
-    if (N == 0) return;
-
-    ScoreParams p{};
+    if (!c.ok()) return c.err;
+    p = ScoreParams{};
     p.q_idx = q_idx->data; p.q_sn = q_idx->stride[0];
     p.index_k = index_k->data; p.k_sp = index_k->stride[0]; p.k_sb = index_k->stride[1];
     p.bt = (const int32_t *)block_table->data;
@@ -149,29 +156,159 @@ void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
     p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB;
     p.P = (int32_t)index_k->shape[0];
     p.idx_scale = idx_scale;
-    if (launch_score(p, etype(q_idx->dtype), etype(index_k->dtype), (int)Di, stream) != hipSuccess)
-        set_error(MSA_ERR_LAUNCH);
+    return MSA_OK;
 }
 
-void msa_select_topk(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
-                     hipStream_t stream) {
+int32_t prep_topk(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx, TopkParams &p) {
     Check c;
     desc(c, scores, 2);
     desc(c, topk_idx, 2);
     dtype_in(c, scores, {MSA_F32});
     dtype_in(c, topk_idx, {MSA_I32});
-    if (!c.ok()) { set_error(c.err); return; }
+    if (!c.ok()) return c.err;
     const int64_t N = scores->shape[0], MB = scores->shape[1];
     if (MB < 1 || MB > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
     if (k < 1 || k > MB) c.fail(MSA_ERR_ARG);
     if (topk_idx->shape[0] != N || topk_idx->shape[1] != k) c.fail(MSA_ERR_SHAPE);
     if (!fits_i32(N)) c.fail(MSA_ERR_UNSUPPORTED);
-    if (!c.ok()) { set_error(c.err); return; }
-    if (N == 0) return;
-    TopkParams p{};
+    if (!c.ok()) return c.err;
+    p = TopkParams{};
     p.scores = (const float *)scores->data; p.sc_sn = scores->stride[0]; p.sc_sj = scores->stride[1];
     p.topk = (int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
     p.N = (int32_t)N; p.MB = (int32_t)MB; p.k = k;
+    return MSA_OK;
+}
+
+// Validates the attention arguments and fills p except the workspace pointers.
+int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tensor *v_cache,
+                  const msa_tensor *block_table, const msa_tensor *seq_lens, const msa_tensor *topk_idx,
+                  int32_t tokens_per_row, msa_tensor *out, float sm_scale, float k_scale, float v_scale,
+                  int32_t block_size, AttnParams &p, AttnPlan &plan, int &qt, int &kvt, int &D) {
+    Check c;
+    desc(c, q, 3);
+    desc(c, k_cache, 4);
+    desc(c, v_cache, 4);
+    desc(c, topk_idx, 2);
+    desc(c, out, 3);
+    paging(c, block_table, seq_lens);
+    dtype_in(c, q, {MSA_BF16, MSA_F32});
+    dtype_in(c, k_cache, {MSA_FP8_E4M3FN, MSA_F32});
+    dtype_in(c, topk_idx, {MSA_I32});
+    dtype_in(c, out, {MSA_BF16, MSA_F32});
+    if (!c.ok()) return c.err;
+    if (v_cache->dtype != k_cache->dtype) c.fail(MSA_ERR_DTYPE);
+    if (block_size != kBlock) c.fail(MSA_ERR_UNSUPPORTED);
+    if (tokens_per_row < 1) c.fail(MSA_ERR_ARG);
+    if (!isfinite(sm_scale) || !isfinite(k_scale) || !isfinite(v_scale)) c.fail(MSA_ERR_ARG);
+    const int64_t R = block_table->shape[0], MB = block_table->shape[1];
+    const int64_t N = R * (int64_t)tokens_per_row;
+    const int64_t Hq = q->shape[1];
+    D = (int)q->shape[2];
+    const int64_t P = k_cache->shape[0], Hkv = k_cache->shape[2];
+    const int64_t K = topk_idx->shape[1];
+    if (q->shape[0] != N || topk_idx->shape[0] != N) c.fail(MSA_ERR_SHAPE);
+    if (k_cache->shape[1] != kBlock || k_cache->shape[3] != D) c.fail(MSA_ERR_SHAPE);
+    for (int i = 0; i < 4; ++i)
+        if (v_cache->shape[i] != k_cache->shape[i]) c.fail(MSA_ERR_SHAPE);
+    if (out->shape[0] != N || out->shape[1] != Hq || out->shape[2] != D) c.fail(MSA_ERR_SHAPE);
+    if (Hkv < 1 || Hq < 1 || Hq % Hkv) c.fail(MSA_ERR_SHAPE);
+    if (K < 1) c.fail(MSA_ERR_SHAPE);
+    if (!c.ok()) return c.err;
+    qt = etype(q->dtype);
+    kvt = etype(k_cache->dtype);
+    if (!attention_supported(qt, kvt, D, (int)(Hq / Hkv))) c.fail(MSA_ERR_UNSUPPORTED);
+    if (!fits_i32(N) || !fits_i32(P) || K > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
+    rows16(c, q);
+    rows16(c, k_cache);
+    rows16(c, v_cache);
+    if (!c.ok()) return c.err;
+    p = AttnParams{};
+    p.q = q->data; p.q_sn = q->stride[0]; p.q_sh = q->stride[1];
+    p.k_cache = k_cache->data;
+    p.k_sp = k_cache->stride[0]; p.k_sb = k_cache->stride[1]; p.k_sh = k_cache->stride[2];
+    p.v_cache = v_cache->data;
+    p.v_sp = v_cache->stride[0]; p.v_sb = v_cache->stride[1]; p.v_sh = v_cache->stride[2];
+    p.bt = (const int32_t *)block_table->data;
+    p.bt_sr = block_table->stride[0]; p.bt_sj = block_table->stride[1];
+    p.seq_lens = (const int32_t *)seq_lens->data; p.sl_s = seq_lens->stride[0];
+    p.topk = (const int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
+    p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
+    p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
+    plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kvt);
+    p.splits = plan.splits;
+    p.bpw = plan.bpw;
+    p.sm_scale = sm_scale; p.k_scale = k_scale; p.v_scale = v_scale;
+    p.out = out->data; p.o_sn = out->stride[0]; p.o_sh = out->stride[1]; p.o_sd = out->stride[2];
+    p.out_bf16 = out->dtype == MSA_BF16;
+    return MSA_OK;
+}
+
+#ifndef MSA_STEP_MERGE_IN_KERNEL
+#define MSA_STEP_MERGE_IN_KERNEL 0
+#endif
+// splits merged inside the attention launch (else by the merge kernel)
+constexpr bool kStepMergeInKernel = MSA_STEP_MERGE_IN_KERNEL;
+
+// the merge kernel over the split partials an attention launch left (none
+// when the MFMA path ran with one split: it writes the output directly)
+int32_t run_merge(const AttnParams &p, const AttnPlan &plan, int D, hipStream_t stream) {
+    if (plan.mfma && p.splits == 1) return MSA_OK;
+    ReduceParams rp{};
+    rp.part_m = p.part_m; rp.part_l = p.part_l; rp.part_acc = p.part_acc;
+    rp.out = p.out; rp.o_sn = p.o_sn; rp.o_sh = p.o_sh; rp.o_sd = p.o_sd;
+    rp.N = p.R * p.T; rp.Hq = p.Hq; rp.D = D; rp.splits = p.splits;
+    rp.out_bf16 = p.out_bf16;
+    rp.v_scale = p.v_scale;
+    return launch_reduce(rp, stream) == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+}
+
+// attention + merge with the workspace already carved
+int32_t run_attn(AttnParams &p, const AttnPlan &plan, int qt, int kvt, int D, hipStream_t stream) {
+    if (launch_attention(p, qt, kvt, D, stream) != hipSuccess) return MSA_ERR_LAUNCH;
+    return run_merge(p, plan, D, stream);
+}
+
+// selection + attention + merge.  On the MFMA path with MB <= 128 the
+// selection runs inside the attention launch: each workgroup selects its
+// token's blocks from the score row (the same wave-level select as the top-k
+// kernel) and one of them stores topk_idx; otherwise the top-k kernel runs
+// first.
+int32_t run_select_attn(const TopkParams &tk, AttnParams &at, const AttnPlan &plan, int qt, int kvt,
+                        int D, hipStream_t stream) {
+    if (plan.mfma && tk.MB <= kSelectInAttnMaxMB) {
+        at.scores = tk.scores; at.sc_sn = tk.sc_sn; at.sc_sj = tk.sc_sj;
+        at.topk_out = tk.topk;
+        const bool merge = kStepMergeInKernel && at.splits > 1;
+        if (launch_attention_select(at, D, merge, stream) != hipSuccess) return MSA_ERR_LAUNCH;
+        return merge ? MSA_OK : run_merge(at, plan, D, stream);
+    }
+    if (launch_topk(tk, stream) != hipSuccess) return MSA_ERR_LAUNCH;
+    return run_attn(at, plan, qt, kvt, D, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
+                     const msa_tensor *block_table, const msa_tensor *seq_lens,
+                     int32_t tokens_per_row, int32_t block_size, float idx_scale,
+                     msa_tensor *scores, hipStream_t stream) {
+    ScoreParams p;
+    int qt, kt, Di;
+    const int32_t e = prep_score(q_idx, index_k, block_table, seq_lens, tokens_per_row, block_size,
+                                 idx_scale, scores, p, qt, kt, Di);
+    if (e != MSA_OK) { set_error(e); return; }
+    if (p.R == 0) return;
+    if (launch_score(p, qt, kt, Di, stream) != hipSuccess) set_error(MSA_ERR_LAUNCH);
+}
+
+void msa_select_topk(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
+                     hipStream_t stream) {
+    TopkParams p;
+    const int32_t e = prep_topk(scores, k, topk_idx, p);
+    if (e != MSA_OK) { set_error(e); return; }
+    if (p.N == 0) return;
     if (launch_topk(p, stream) != hipSuccess) set_error(MSA_ERR_LAUNCH);
 }
 
@@ -189,83 +326,92 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
                        int32_t tokens_per_row, msa_tensor *out,
                        float sm_scale, float k_scale, float v_scale, int32_t block_size,
                        void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    Check c;
-    desc(c, q, 3);
-    desc(c, k_cache, 4);
-    desc(c, v_cache, 4);
-    desc(c, topk_idx, 2);
-    desc(c, out, 3);
-    paging(c, block_table, seq_lens);
-    dtype_in(c, q, {MSA_BF16, MSA_F32});
-    dtype_in(c, k_cache, {MSA_FP8_E4M3FN, MSA_F32});
-    dtype_in(c, topk_idx, {MSA_I32});
-    dtype_in(c, out, {MSA_BF16, MSA_F32});
-    if (!c.ok()) { set_error(c.err); return; }
-    if (v_cache->dtype != k_cache->dtype) c.fail(MSA_ERR_DTYPE);
-    if (block_size != kBlock) c.fail(MSA_ERR_UNSUPPORTED);
-    if (tokens_per_row < 1) c.fail(MSA_ERR_ARG);
-    if (!isfinite(sm_scale) || !isfinite(k_scale) || !isfinite(v_scale)) c.fail(MSA_ERR_ARG);
-    const int64_t R = block_table->shape[0], MB = block_table->shape[1];
-    const int64_t N = R * (int64_t)tokens_per_row;
-    const int64_t Hq = q->shape[1], D = q->shape[2];
-    const int64_t P = k_cache->shape[0], Hkv = k_cache->shape[2];
-    const int64_t K = topk_idx->shape[1];
-    if (q->shape[0] != N || topk_idx->shape[0] != N) c.fail(MSA_ERR_SHAPE);
-    if (k_cache->shape[1] != kBlock || k_cache->shape[3] != D) c.fail(MSA_ERR_SHAPE);
-    for (int i = 0; i < 4; ++i)
-        if (v_cache->shape[i] != k_cache->shape[i]) c.fail(MSA_ERR_SHAPE);
-    if (out->shape[0] != N || out->shape[1] != Hq || out->shape[2] != D) c.fail(MSA_ERR_SHAPE);
-    if (Hkv < 1 || Hq < 1 || Hq % Hkv) c.fail(MSA_ERR_SHAPE);
-    if (K < 1) c.fail(MSA_ERR_SHAPE);
-    if (!c.ok()) { set_error(c.err); return; }
-    if (!attention_supported(etype(q->dtype), etype(k_cache->dtype), (int)D, (int)(Hq / Hkv)))
-        c.fail(MSA_ERR_UNSUPPORTED);
-    if (!fits_i32(N) || !fits_i32(P) || K > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
-    rows16(c, q);
-    rows16(c, k_cache);
-    rows16(c, v_cache);
-    if (!c.ok()) { set_error(c.err); return; }
+    AttnParams p;
+    AttnPlan plan;
+    int qt, kvt, D;
+    const int32_t e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row,
+                                out, sm_scale, k_scale, v_scale, block_size, p, plan, qt, kvt, D);
+    if (e != MSA_OK) { set_error(e); return; }
+    const int32_t N = p.R * p.T;
     if (N == 0) return;
-    const size_t need = attn_workspace_bytes((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv,
-                                             (int32_t)D, (int32_t)K);
+    const size_t need = attn_workspace_bytes(p.R, p.T, p.Hq, p.Hkv, D, p.k);
     if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) {
         set_error(MSA_ERR_WORKSPACE);
         return;
     }
+    attn_carve_workspace(workspace, p.splits, N, p.Hq, p.Hkv, D, &p.part_m, &p.part_l, &p.part_acc,
+                         &p.counters);
+    const int32_t r = run_attn(p, plan, qt, kvt, D, stream);
+    if (r != MSA_OK) set_error(r);
+}
 
-    AttnParams p{};
-    p.q = q->data; p.q_sn = q->stride[0]; p.q_sh = q->stride[1];
-    p.k_cache = k_cache->data;
-    p.k_sp = k_cache->stride[0]; p.k_sb = k_cache->stride[1]; p.k_sh = k_cache->stride[2];
-    p.v_cache = v_cache->data;
-    p.v_sp = v_cache->stride[0]; p.v_sb = v_cache->stride[1]; p.v_sh = v_cache->stride[2];
-    p.bt = (const int32_t *)block_table->data;
-    p.bt_sr = block_table->stride[0]; p.bt_sj = block_table->stride[1];
-    p.seq_lens = (const int32_t *)seq_lens->data; p.sl_s = seq_lens->stride[0];
-    p.topk = (const int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
-    p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
-    p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
-    const int qt = etype(q->dtype), kt = etype(k_cache->dtype);
-    const AttnPlan plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kt);
-    p.splits = plan.splits;
-    p.bpw = plan.bpw;
-    p.sm_scale = sm_scale; p.k_scale = k_scale; p.v_scale = v_scale;
-    attn_carve_workspace(workspace, p.splits, (int32_t)N, (int32_t)Hq, (int32_t)Hkv, (int32_t)D,
-                         &p.part_m, &p.part_l, &p.part_acc, &p.counters);
-    p.out = out->data; p.o_sn = out->stride[0]; p.o_sh = out->stride[1]; p.o_sd = out->stride[2];
-    p.out_bf16 = out->dtype == MSA_BF16;
-    if (launch_attention(p, qt, kt, (int)D, stream) != hipSuccess) {
-        set_error(MSA_ERR_LAUNCH);
+size_t msa_decode_step_workspace_bytes(int32_t rows, int32_t tokens_per_row, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t k) {
+    return msa_sparse_decode_workspace_bytes(rows, tokens_per_row, num_q_heads, num_kv_heads, head_dim, k);
+}
+
+void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
+                              const msa_tensor *q, const msa_tensor *k_cache,
+                              const msa_tensor *v_cache, const msa_tensor *block_table,
+                              const msa_tensor *seq_lens, int32_t tokens_per_row, msa_tensor *out,
+                              float sm_scale, float k_scale, float v_scale, int32_t block_size,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    TopkParams tk;
+    AttnParams at;
+    AttnPlan plan;
+    int qt, kvt, D;
+    int32_t e = prep_topk(scores, k, topk_idx, tk);
+    if (e == MSA_OK)
+        e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row, out, sm_scale,
+                      k_scale, v_scale, block_size, at, plan, qt, kvt, D);
+    if (e == MSA_OK && (scores->shape[0] != (int64_t)at.R * at.T || scores->shape[1] != at.MB))
+        e = MSA_ERR_SHAPE;
+    if (e != MSA_OK) { set_error(e); return; }
+    const int32_t N = at.R * at.T;
+    if (N == 0) return;
+    const size_t need = attn_workspace_bytes(at.R, at.T, at.Hq, at.Hkv, D, k);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) {
+        set_error(MSA_ERR_WORKSPACE);
         return;
     }
-    if (plan.mfma) return;                       // the MFMA path merges its splits itself
-    ReduceParams rp{};
-    rp.part_m = p.part_m; rp.part_l = p.part_l; rp.part_acc = p.part_acc;
-    rp.out = out->data; rp.o_sn = out->stride[0]; rp.o_sh = out->stride[1]; rp.o_sd = out->stride[2];
-    rp.N = (int32_t)N; rp.Hq = (int32_t)Hq; rp.D = (int32_t)D; rp.splits = p.splits;
-    rp.out_bf16 = out->dtype == MSA_BF16;
-    rp.v_scale = v_scale;
-    if (launch_reduce(rp, stream) != hipSuccess) set_error(MSA_ERR_LAUNCH);
+    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_m, &at.part_l,
+                         &at.part_acc, &at.counters);
+    const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);
+    if (r != MSA_OK) set_error(r);
+}
+
+void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const msa_tensor *q,
+                     const msa_tensor *k_cache, const msa_tensor *v_cache,
+                     const msa_tensor *block_table, const msa_tensor *seq_lens,
+                     int32_t tokens_per_row, int32_t k, int32_t block_size,
+                     float idx_scale, float sm_scale, float k_scale, float v_scale,
+                     msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    ScoreParams sc;
+    TopkParams tk;
+    AttnParams at;
+    AttnPlan plan;
+    int qit, kit, Di, qt, kvt, D;
+    int32_t e = prep_score(q_idx, index_k, block_table, seq_lens, tokens_per_row, block_size, idx_scale,
+                           scores, sc, qit, kit, Di);
+    if (e == MSA_OK) e = prep_topk(scores, k, topk_idx, tk);
+    if (e == MSA_OK)
+        e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row, out, sm_scale,
+                      k_scale, v_scale, block_size, at, plan, qt, kvt, D);
+    if (e == MSA_OK && k_cache->shape[0] != index_k->shape[0]) e = MSA_ERR_SHAPE;
+    if (e != MSA_OK) { set_error(e); return; }
+    const int32_t N = sc.R * sc.T;
+    if (N == 0) return;
+    const size_t need = attn_workspace_bytes(sc.R, sc.T, at.Hq, at.Hkv, D, k);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) {
+        set_error(MSA_ERR_WORKSPACE);
+        return;
+    }
+    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_m, &at.part_l,
+                         &at.part_acc, &at.counters);
+    if (launch_score(sc, qit, kit, Di, stream) != hipSuccess) { set_error(MSA_ERR_LAUNCH); return; }
+    const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);
+    if (r != MSA_OK) set_error(r);
 }
 
 }  // extern "C"

@@ -10,6 +10,7 @@ constexpr int kBlock = 128;          // tokens per page (vLLM design note: block
 constexpr int kMaxMB = 2048;         // logical blocks per row served by select/attention
 constexpr int kTokGroup = 4;         // query tokens of one row handled together
 constexpr int kSplitTargetWGs = 256; // attention workgroups aimed for (one per CU)
+constexpr int kCounterStride = 64;   // int32s between split-arrival counters (one per 256 B)
 
 enum ElemType { E_F32 = 0, E_BF16 = 1, E_FP8 = 2, E_I32 = 3 };
 
@@ -36,13 +37,16 @@ struct AttnParams {
     const int32_t *bt;   int64_t bt_sr, bt_sj;
     const int32_t *seq_lens; int64_t sl_s;
     const int32_t *topk; int64_t tk_sn, tk_si;     // [N, k]
+    // selection computed in the attention kernel: score sheet in, topk out
+    const float *scores; int64_t sc_sn, sc_sj;     // [N, MB]
+    int32_t *topk_out;                             // same strides as topk
     int32_t R, T, MB, P, Hq, Hkv, k;
     int32_t splits;                                // S
     int32_t bpw;                                   // selected pages per wave (token path)
     float sm_scale, k_scale, v_scale;
     // split-K partials (workspace): m, l [S, N, Hq]; acc [S, N, Hq, D]
     float *part_m, *part_l, *part_acc;
-    int32_t *counters;                             // [N, Hkv], zero between calls
+    int32_t *counters;                             // [N, Hkv] x kCounterStride, zero between calls
     void *out; int64_t o_sn, o_sh, o_sd;           // [N, Hq, D] (token path writes it)
     int32_t out_bf16;
 };
@@ -54,6 +58,13 @@ struct ReduceParams {
     int32_t out_bf16;
     float v_scale;
 };
+
+// Attention that computes each token's selection from the score sheet first
+// (the decode step's second launch); MB <= 128.  merge: the splits are merged
+// in the same launch through the workspace counters (else the merge kernel
+// must follow when splits > 1).
+hipError_t launch_attention_select(const AttnParams &p, int D, bool merge, hipStream_t s);
+constexpr int kSelectInAttnMaxMB = 128;
 
 // Split plan of msa_sparse_decode for the given sizes and element types.
 struct AttnPlan {

@@ -18,21 +18,13 @@
 //    v_mfma_f32_16x16x32_bf16 after exact FP8 -> bf16 decoding.
 #include "device_util.h"
 #include "msa_internal.h"
+#include "score_unit.h"
 
 namespace msa {
 
 namespace {
 
-__device__ __forceinline__ int clamp_len(int L, int MB) {
-    return max(0, min(L, MB * kBlock));
-}
 
-// 16-byte load with the non-temporal cache policy (index pages are read once)
-__device__ __forceinline__ uint4 load_nt16(const uint8_t *ptr) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    const u32x4 v = __builtin_nontemporal_load((const u32x4 *)ptr);
-    return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // ------------------------------------------------------------------ VALU path
 
@@ -187,85 +179,15 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
 }
 
 // ------------------------------------------------------------- MFMA decode path
-//
-// Decode rows (T <= 16 tokens): one wave per (row, page).  The row's T query
-// tokens are the 16 columns of v_mfma_f32_16x16x32_bf16 (unused columns are
-// zero); the page's 128 keys are its rows.  Each lane pulls its operand bytes
-// straight from HBM -- key 16*kt + lane%16, Di/4 contiguous bytes at
-// d = (Di/4)*(lane/16) -- so a wave keeps the whole 16 KiB page in flight in
-// 64 registers, and the VALU only decodes FP8 -> bf16 (exact) and takes the
-// masked running max.  The dot products themselves run on the matrix cores.
 
 template <int DI>
 __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
-    constexpr int KS = DI / 32;                 // k-steps per 16-key tile
-    constexpr int LB = DI / 4;                  // bytes per lane per key row
-    constexpr int NL = LB / 16;                 // 16-byte loads per key tile
-    static_assert(NL >= 1, "index dim");
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int grp = lane >> 4, li = lane & 15;
+    const int wave = threadIdx.x >> 6;
     const int JC = (p.MB + 3) >> 2;
     const int r = blockIdx.x / JC;
     const int j = (blockIdx.x % JC) * 4 + wave;
     if (j >= p.MB) return;                      // no barriers in this kernel
-    const int L = clamp_len(p.seq_lens[(int64_t)r * p.sl_s], p.MB);
-    const int vmax = max(0, L);                 // the row's last token sees L keys
-    const int64_t n0 = (int64_t)r * p.T;
-    const bool tok = li < p.T;
-    const int vt = tok ? max(0, L - (p.T - 1 - li)) : 0;
-    float best = -INFINITY;
-    bool bad_page = false;
-    if (j * kBlock < vmax) {
-        const int pid = p.bt[(int64_t)r * p.bt_sr + (int64_t)j * p.bt_sj];
-        if (pid < 0 || pid >= p.P) {
-            bad_page = true;
-        } else {
-            const uint8_t *pg = (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp;
-            uint4 kf[8][NL];
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-                for (int h = 0; h < NL; ++h)
-                    kf[kt][h] = load_nt16(pg + (int64_t)(kt * 16 + li) * p.k_sb + LB * grp + 16 * h);
-            // B operand: token li, d = LB*grp + 8*ks .. +8 (bf16)
-            uint4 qf[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                qf[ks] = tok ? *(const uint4 *)((const uint16_t *)p.q_idx + (n0 + li) * p.q_sn + LB * grp + 8 * ks)
-                             : make_uint4(0, 0, 0, 0);
-            }
-            const int kbase = j * kBlock;
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const uint4 raw = kf[kt][ks >> 1];
-                    const uint32_t lo = (ks & 1) ? raw.z : raw.x, hi = (ks & 1) ? raw.w : raw.y;
-                    uint4 a;
-                    a.x = fp8x2_to_bf16x2<false>(lo); a.y = fp8x2_to_bf16x2<true>(lo);
-                    a.z = fp8x2_to_bf16x2<false>(hi); a.w = fp8x2_to_bf16x2<true>(hi);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                  __builtin_bit_cast(bf16x8, qf[ks]), acc, 0, 0, 0);
-                }
-                // acc[e] = dot of key 16*kt + 4*grp + e with token li
-                if (kbase + kBlock <= vt) {                 // whole page visible to this token
-                    best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int pos = kbase + kt * 16 + 4 * grp + e;
-                        best = (pos < vt) ? fmaxf(best, acc[e]) : best;
-                    }
-                }
-            }
-            best = max_across_groups<16>(best);
-        }
-    }
-    if (grp == 0 && tok) {
-        const float v = bad_page ? __builtin_nanf("") : best * p.idx_scale;
-        p.scores[(n0 + li) * p.sc_sn + (int64_t)j * p.sc_sj] = v;
-    }
+    score_page<DI>(p, r, j);
 }
 
 // ------------------------------------------------------------------ MFMA path

@@ -93,8 +93,10 @@ typedef enum msa_status {
  *   idx_scale   > 0, finite (static per-tensor dequantisation scale)
  *   scores      [N, MB]     f32 OUT         any strides
  * Di must be 32, 64 or 128.  A visible block whose physical page id lies
- * outside [0, P) scores NaN (the page is not read).  Queries with T >= 16
- * per row run on MFMA tiles; smaller T on vector ALUs.
+ * outside [0, P) scores NaN (the page is not read).  With bf16 queries, an FP8
+ * index and Di in {64, 128} the dot products run on bf16 MFMA tiles (one page
+ * per wave for rows of up to 16 tokens, 128-query tiles beyond); otherwise on
+ * vector ALUs in fp32.
  */
 void msa_block_score(const msa_tensor *q_idx, const msa_tensor *index_k,
                      const msa_tensor *block_table, const msa_tensor *seq_lens,
@@ -166,6 +168,54 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
                        int32_t tokens_per_row, msa_tensor *out,
                        float sm_scale, float k_scale, float v_scale, int32_t block_size,
                        void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Stages 2 and 3 in one call: msa_select_topk(scores, k, topk_idx), then
+ * msa_sparse_decode over that selection, with the same arguments, domain and
+ * bit-identical outputs (topk_idx and out are both written).  For callers that
+ * hold a score sheet already.  When the attention runs on MFMA (bf16 queries,
+ * FP8 caches, Hq/Hkv = 16) and MB <= 128 the selection is not a launch of its
+ * own: each attention workgroup selects its token's blocks from the score row
+ * with the same wave-level radix select as msa_select_topk, and one of them
+ * stores topk_idx; otherwise the top-k kernel runs first.
+ *
+ *   scores      [N, MB] f32, N = R * tokens_per_row, MB = block_table's width
+ *   workspace   as for msa_sparse_decode (same size query, same contract)
+ */
+void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
+                              const msa_tensor *q, const msa_tensor *k_cache,
+                              const msa_tensor *v_cache, const msa_tensor *block_table,
+                              const msa_tensor *seq_lens, int32_t tokens_per_row, msa_tensor *out,
+                              float sm_scale, float k_scale, float v_scale, int32_t block_size,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes msa_decode_step needs for these sizes (the same as
+ * msa_sparse_decode_workspace_bytes).  Depends on the sizes only.
+ */
+size_t msa_decode_step_workspace_bytes(int32_t rows, int32_t tokens_per_row,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t k);
+
+/*
+ * The three stages in one call: msa_block_score, then msa_select_sparse_decode
+ * with width k (msa_select_topk, then msa_sparse_decode), with the same
+ * arguments, the same domain and bit-identical outputs (scores, topk_idx and
+ * out are all written).
+ *
+ *   index_k and k_cache/v_cache must have the same pool size P.
+ *   workspace   at least msa_decode_step_workspace_bytes(...) bytes, 256-byte
+ *               aligned, zero-filled once before first use; every call leaves
+ *               its counters at zero again.  Calls sharing a workspace must
+ *               not run concurrently.
+ */
+void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const msa_tensor *q,
+                     const msa_tensor *k_cache, const msa_tensor *v_cache,
+                     const msa_tensor *block_table, const msa_tensor *seq_lens,
+                     int32_t tokens_per_row, int32_t k, int32_t block_size,
+                     float idx_scale, float sm_scale, float k_scale, float v_scale,
+                     msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
+                     void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Error code recorded by the most recent failing call on this thread, then
  * reset to MSA_OK.  Returns MSA_OK when no call failed since the last read. */

@@ -139,3 +139,43 @@ def test_sparse_decode_rejects(msa):
     msa.lib.msa_select_topk(None, 4, ctypes.byref(dt), None)
     assert msa.lib.msa_get_last_error() == 1
     assert torch.isnan(c["out"].float()).all()
+
+
+def test_select_sparse_decode_rejects(msa):
+    c = _cpu_case()
+    f = msa.msa_select_sparse_decode
+    base = [c["scores"], 4, c["topk"], c["q"], c["k_cache"], c["v_cache"], c["block_table"],
+            c["seq_lens"], 4, c["out"], 0.088, 0.01, 0.01, 128, c["ws"]]
+
+    def with_(i, v):
+        a = list(base)
+        a[i] = v
+        return a
+
+    _expect(msa, 7, f, *with_(1, 0))                                      # k < 1
+    _expect(msa, 3, f, *with_(2, torch.zeros(8, 3, dtype=torch.int32)))   # topk width != k
+    _expect(msa, 3, f, *with_(0, torch.zeros(8, 9)))                      # scores width != MB
+    _expect(msa, 3, f, *with_(0, torch.zeros(6, 8)))                      # scores rows != N
+    _expect(msa, 6, f, *with_(14, c["ws"][:1024]))                        # workspace too small
+    _expect(msa, 2, f, *with_(0, c["scores"].double()))
+    assert (c["topk"] == -7).all() and torch.isnan(c["out"].float()).all()
+
+
+def test_decode_step_rejects(msa):
+    c = _cpu_case()
+    f = msa.msa_decode_step
+    base = [c["q_idx"], c["index_k"], c["q"], c["k_cache"], c["v_cache"], c["block_table"],
+            c["seq_lens"], 4, 4, 128, 0.01, 0.088, 0.01, 0.01, c["scores"], c["topk"], c["out"],
+            c["ws"]]
+
+    def with_(i, v):
+        a = list(base)
+        a[i] = v
+        return a
+
+    _expect(msa, 3, f, *with_(3, torch.zeros(21, 128, 1, 128, dtype=torch.uint8)))  # pool sizes differ
+    _expect(msa, 7, f, *with_(8, 9))                                      # k > MB
+    _expect(msa, 6, f, *with_(17, c["ws"][:1024]))
+    _expect(msa, 5, f, *with_(9, 64))                                     # block size
+    assert torch.isnan(c["scores"]).all() and (c["topk"] == -7).all()
+    assert torch.isnan(c["out"].float()).all()
