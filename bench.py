@@ -36,8 +36,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# the launches msa_select_sparse_decode makes at this shape
-ROOFLINE_KERNEL = "attn_token_select_kernel<128,false> + attn_reduce_kernel"
+# the launch msa_select_sparse_decode makes at this shape
+ROOFLINE_KERNEL = "attn_token_select_kernel<128>"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 

@@ -243,18 +243,12 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     return MSA_OK;
 }
 
-#ifndef MSA_STEP_MERGE_IN_KERNEL
-#define MSA_STEP_MERGE_IN_KERNEL 0
-#endif
-// splits merged inside the attention launch (else by the merge kernel)
-constexpr bool kStepMergeInKernel = MSA_STEP_MERGE_IN_KERNEL;
-
-// the merge kernel over the split partials an attention launch left (none
-// when the MFMA path ran with one split: it writes the output directly)
+// the merge kernel over the split partials the VALU attention launch left
+// (the MFMA launch merges its splits itself)
 int32_t run_merge(const AttnParams &p, const AttnPlan &plan, int D, hipStream_t stream) {
-    if (plan.mfma && p.splits == 1) return MSA_OK;
+    if (plan.mfma) return MSA_OK;
     ReduceParams rp{};
-    rp.part_m = p.part_m; rp.part_l = p.part_l; rp.part_acc = p.part_acc;
+    rp.part_ml = p.part_ml; rp.part_acc = p.part_acc;
     rp.out = p.out; rp.o_sn = p.o_sn; rp.o_sh = p.o_sh; rp.o_sd = p.o_sd;
     rp.N = p.R * p.T; rp.Hq = p.Hq; rp.D = D; rp.splits = p.splits;
     rp.out_bf16 = p.out_bf16;
@@ -278,9 +272,7 @@ int32_t run_select_attn(const TopkParams &tk, AttnParams &at, const AttnPlan &pl
     if (plan.mfma && tk.MB <= kSelectInAttnMaxMB) {
         at.scores = tk.scores; at.sc_sn = tk.sc_sn; at.sc_sj = tk.sc_sj;
         at.topk_out = tk.topk;
-        const bool merge = kStepMergeInKernel && at.splits > 1;
-        if (launch_attention_select(at, D, merge, stream) != hipSuccess) return MSA_ERR_LAUNCH;
-        return merge ? MSA_OK : run_merge(at, plan, D, stream);
+        return launch_attention_select(at, D, stream) == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
     }
     if (launch_topk(tk, stream) != hipSuccess) return MSA_ERR_LAUNCH;
     return run_attn(at, plan, qt, kvt, D, stream);
@@ -339,7 +331,7 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
         set_error(MSA_ERR_WORKSPACE);
         return;
     }
-    attn_carve_workspace(workspace, p.splits, N, p.Hq, p.Hkv, D, &p.part_m, &p.part_l, &p.part_acc,
+    attn_carve_workspace(workspace, p.splits, N, p.Hq, p.Hkv, D, &p.part_ml, &p.part_acc,
                          &p.counters);
     const int32_t r = run_attn(p, plan, qt, kvt, D, stream);
     if (r != MSA_OK) set_error(r);
@@ -374,7 +366,7 @@ void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *t
         set_error(MSA_ERR_WORKSPACE);
         return;
     }
-    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_m, &at.part_l,
+    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_ml,
                          &at.part_acc, &at.counters);
     const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);
     if (r != MSA_OK) set_error(r);
@@ -407,7 +399,7 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
         set_error(MSA_ERR_WORKSPACE);
         return;
     }
-    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_m, &at.part_l,
+    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_ml,
                          &at.part_acc, &at.counters);
     if (launch_score(sc, qit, kit, Di, stream) != hipSuccess) { set_error(MSA_ERR_LAUNCH); return; }
     const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);

@@ -116,21 +116,9 @@ __device__ __forceinline__ void split_range(int U, int S, int s, int &beg, int &
 
 // ------------------------------------------------------------------ MFMA path
 //
-// Standalone launch of the per-token MFMA attention unit (attn_unit.h): one
-// workgroup per (query token n, KV head g, split s of n's selection list);
-// wave w of the workgroup takes selection entries s*4*bpw + w*bpw .. +bpw.
-// A wave's K and V pages go straight from HBM into the wave's LDS slots
-// (direct-to-LDS 16-byte loads, 16-byte chunks XOR-swizzled by key); QK^T
-// reads K rows as MFMA A operands, PV reads V back with ds_read_b64_tr_b8,
-// which hands each lane 8 keys at one d: the A operand of O^T = V^T P^T.
-// The 4 waves merge their softmax partials in LDS; the splits of a token merge
-// through a per-(token, KV head) arrival counter in the workspace: the last
-// workgroup to arrive combines the S partials in a fixed order and writes the
-// output, then resets the counter to zero (so the counters are zero again
-// after every call).  Workgroups are placed so that all those of a row (at
-// least 8 rows) or of a token run on one XCD and share its L2: a page chosen
-// by several of a row's tokens is then fetched from HBM once.  Correctness
-// does not depend on the placement (the hand-off is device-coherent).
+// Launches of the per-token MFMA attention unit (attn_unit.h, which describes
+// the chunk pipeline and the split merge): one workgroup per (query token n,
+// KV head g, split s of n's selection list), placed by decode_token_slot.
 
 struct TokenSlot {
     int n, g, s;
@@ -169,22 +157,18 @@ __device__ __forceinline__ TokenSlot decode_token_slot(const AttnParams &p) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256, 1) void attn_token_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4][2 * kBlock * D];
+__global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_token_kernel(AttnParams p) {
     const TokenSlot q = decode_token_slot(p);
     if (!q.live) return;                         // uniform over the workgroup
-    attn_unit<D, false, false>(p, lds, q.n, q.g, q.s);
+    attn_unit<D, false>(p, q.n, q.g, q.s);
 }
 
-// The same, selecting the token's blocks from its score row first (MB <= 128);
-// MERGE: the splits are merged in this launch (no merge kernel).
-template <int D, bool MERGE>
-__global__ __launch_bounds__(256, 1) void attn_token_select_kernel(AttnParams p) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[4][2 * kBlock * D];
-    __shared__ int slots[4][kSelSlots];
+// The same, selecting the token's blocks from its score row first (MB <= 128).
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_token_select_kernel(AttnParams p) {
     const TokenSlot q = decode_token_slot(p);
     if (!q.live) return;
-    attn_unit<D, MERGE, true>(p, lds, q.n, q.g, q.s, slots);
+    attn_unit<D, true>(p, q.n, q.g, q.s);
 }
 
 // ------------------------------------------------------------------ VALU path
@@ -293,14 +277,17 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
         }
     }
     if (!tok_active) return;
+    const int64_t N = (int64_t)p.R * p.T;
     for (int hh = 0; hh < G; ++hh) {
-        const int64_t row = ((int64_t)q.s * (p.R * p.T) + n) * p.Hq + q.g * G + hh;
+        const int h = q.g * G + hh;
         if (lane == 0) {
-            p.part_m[row] = any ? st_m[w][hh] : -INFINITY;
-            p.part_l[row] = any ? st_l[w][hh] : 0.f;
+            float *ml = p.part_ml + part_ml_index(q.s, n, h, N, p.Hq);
+            ml[0] = any ? st_m[w][hh] : -INFINITY;
+            ml[1] = any ? st_l[w][hh] : 0.f;
         }
         if (any)
-            for (int d = lane; d < D; d += 64) p.part_acc[row * D + d] = st_acc[w][hh][d];
+            for (int d = lane; d < D; d += 64)
+                p.part_acc[part_acc_index(q.s, n, h, d, N, p.Hq, D)] = st_acc[w][hh][d];
     }
 }
 
@@ -311,37 +298,37 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 // in increasing order (deterministic).  A split that saw no key has m = -inf
 // and its acc is never read into the sum.
 __global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
+    // thread -> (token n, 8-wide d group dq, head h), h fastest: the partial
+    // loads of consecutive threads are contiguous
     const int DQ = p.D >> 3;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t NH = (int64_t)p.N * p.Hq;
-    if (idx >= NH * DQ) return;
-    const int dq = (int)(idx % DQ);
-    const int64_t nh = idx / DQ;                  // n * Hq + h
-    const int h = (int)(nh % p.Hq);
-    const int64_t n = nh / p.Hq;
+    const int64_t N = p.N;
+    if (idx >= N * p.Hq * DQ) return;
+    const int h = (int)(idx % p.Hq);
+    const int dq = (int)((idx / p.Hq) % DQ);
+    const int64_t n = idx / ((int64_t)p.Hq * DQ);
     float m2 = -INFINITY, l2 = 0.f, a2[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) a2[e] = 0.f;
     for (int s0 = 0; s0 < p.splits; s0 += 4) {
-        float ms[4], ls[4];
+        f32x2 ml[4];
         f32x4 lo[4], hi[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             const int sp = min(s0 + u, p.splits - 1);
-            const int64_t row = (int64_t)sp * NH + nh;
-            ms[u] = (s0 + u < p.splits) ? p.part_m[row] : -INFINITY;
-            ls[u] = p.part_l[row];
-            const f32x4 *src = (const f32x4 *)(p.part_acc + row * p.D + dq * 8);
+            ml[u] = *(const f32x2 *)(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
+            const f32x4 *src = (const f32x4 *)(p.part_acc + part_acc_index(sp, n, h, dq * 8, N, p.Hq, p.D));
             lo[u] = src[0];
             hi[u] = src[1];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const bool live = ms[u] != -INFINITY;
-            const float mn = fmaxf(m2, ms[u]);
+            const bool live = s0 + u < p.splits && ml[u].x != -INFINITY;
+            const float mu = live ? ml[u].x : -INFINITY;
+            const float mn = fmaxf(m2, mu);
             const float wo = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
-            const float wn = live ? exp2_fast(ms[u] - mn) : 0.f;
-            l2 = l2 * wo + (live ? ls[u] : 0.f) * wn;
+            const float wn = live ? exp2_fast(mu - mn) : 0.f;
+            l2 = l2 * wo + (live ? ml[u].y : 0.f) * wn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 a2[e] = a2[e] * wo + (live ? lo[u][e] : 0.f) * wn;
@@ -382,13 +369,13 @@ static int64_t token_grid(const AttnParams &p) {
 
 template <int D>
 hipError_t launch_token(const AttnParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((attn_token_kernel<D>), dim3((unsigned)token_grid(p)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_token_kernel<D>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
     return hipGetLastError();
 }
 
-template <int D, bool MERGE>
+template <int D>
 hipError_t launch_token_select(const AttnParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((attn_token_select_kernel<D, MERGE>), dim3((unsigned)token_grid(p)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_token_select_kernel<D>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
     return hipGetLastError();
 }
 
@@ -419,7 +406,7 @@ static int union_splits(int32_t R, int32_t T, int32_t Hkv, int32_t k) {
     return (int)(S < 1 ? 1 : S);
 }
 
-// token path: one selected page per wave while k <= 64, 4 waves per workgroup
+// token path: one selected page per pair of waves while k <= 64, 4 pages per workgroup
 static void token_split(int32_t k, int32_t *S, int32_t *bpw) {
     *bpw = (k + 63) / 64;
     *S = (k + 4 * *bpw - 1) / (4 * *bpw);
@@ -443,7 +430,7 @@ AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// [counters N*Hkv x 256 B][m S*N*Hq][l S*N*Hq][acc S*N*Hq*D], each 256-byte aligned.
+// [counters N*Hkv x 256 B][(m, l) S*N*Hq pairs][acc S*N*Hq*D], each 256-byte aligned.
 // The size covers both paths (the query does not know the element types).
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k) {
     int32_t St, bpw;
@@ -452,18 +439,17 @@ size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32
     const size_t S = (size_t)(St > Su ? St : Su);
     const size_t N = (size_t)R * T;
     const size_t rows = S * N * Hq;
-    return N * Hkv * kCounterStride * 4 + 2 * align256(rows * 4) + align256(rows * D * 4);
+    return N * Hkv * kCounterStride * 4 + align256(rows * 8) + align256(rows * D * 4);
 }
 
 void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                          float **m, float **l, float **acc, int32_t **counters) {
+                          float **ml, float **acc, int32_t **counters) {
     const size_t rows = (size_t)S * N * Hq;
     char *b = (char *)ws;
     *counters = (int32_t *)b;
     b += (size_t)N * Hkv * kCounterStride * 4;
-    *m = (float *)b;
-    *l = (float *)(b + align256(rows * 4));
-    *acc = (float *)(b + 2 * align256(rows * 4));
+    *ml = (float *)b;
+    *acc = (float *)(b + align256(rows * 8));
     (void)D;
 }
 
@@ -485,11 +471,10 @@ hipError_t launch_attention(const AttnParams &p, int q_type, int kv_type, int D,
                    : launch_valu_types<128>(p, q_type, kv_type, grid, s);
 }
 
-hipError_t launch_attention_select(const AttnParams &p, int D, bool merge, hipStream_t s) {
+hipError_t launch_attention_select(const AttnParams &p, int D, hipStream_t s) {
     if ((int64_t)p.R * p.T * p.Hkv == 0) return hipSuccess;
     if (p.MB > kSelSlots || p.k > p.MB) return hipErrorInvalidValue;
-    if (merge) return D == 64 ? launch_token_select<64, true>(p, s) : launch_token_select<128, true>(p, s);
-    return D == 64 ? launch_token_select<64, false>(p, s) : launch_token_select<128, false>(p, s);
+    return D == 64 ? launch_token_select<64>(p, s) : launch_token_select<128>(p, s);
 }
 
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s) {

@@ -52,6 +52,20 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
 // only feeds softmax weights; -inf gives 0).
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Compile-time loop: f(Int<I>{}) for I = B .. E-1 (the index can be a template
+// argument inside f).
+template <int I>
+struct Int {
+    static constexpr int value = I;
+};
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(Int<B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 // Lane permutes through DPP (row = 16 lanes).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {

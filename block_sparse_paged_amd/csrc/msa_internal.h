@@ -44,38 +44,52 @@ struct AttnParams {
     int32_t splits;                                // S
     int32_t bpw;                                   // selected pages per wave (token path)
     float sm_scale, k_scale, v_scale;
-    // split-K partials (workspace): m, l [S, N, Hq]; acc [S, N, Hq, D]
-    float *part_m, *part_l, *part_acc;
+    // split-K partials (workspace), see part_ml_index / part_acc_index
+    float *part_ml, *part_acc;
     int32_t *counters;                             // [N, Hkv] x kCounterStride, zero between calls
     void *out; int64_t o_sn, o_sh, o_sd;           // [N, Hq, D] (token path writes it)
     int32_t out_bf16;
 };
 
 struct ReduceParams {
-    const float *part_m, *part_l, *part_acc;
+    const float *part_ml, *part_acc;
     void *out; int64_t o_sn, o_sh, o_sd;           // [N, Hq, D]
     int32_t N, Hq, D, splits;
     int32_t out_bf16;
     float v_scale;
 };
 
+// Split partials in the workspace.  Split s of query token n leaves, per query
+// head h, its running max m (log2 units) and sum l as a pair, and its
+// unnormalised accumulator with the 8 consecutive d of group d/8 of all heads
+// side by side, so that the 16 heads x 8 d one thread group writes are
+// contiguous:
+//   (m, l)       at part_ml[part_ml_index(s, n, h)]     (2 floats)
+//   acc[d]       at part_acc[part_acc_index(s, n, h, d)]
+__host__ __device__ __forceinline__ int64_t part_ml_index(int s, int64_t n, int h, int64_t N, int Hq) {
+    return (((int64_t)s * N + n) * Hq + h) * 2;
+}
+__host__ __device__ __forceinline__ int64_t part_acc_index(int s, int64_t n, int h, int d, int64_t N, int Hq,
+                                                           int D) {
+    return ((((int64_t)s * N + n) * (D / 8) + d / 8) * Hq + h) * 8 + (d & 7);
+}
+
 // Attention that computes each token's selection from the score sheet first
-// (the decode step's second launch); MB <= 128.  merge: the splits are merged
-// in the same launch through the workspace counters (else the merge kernel
-// must follow when splits > 1).
-hipError_t launch_attention_select(const AttnParams &p, int D, bool merge, hipStream_t s);
+// (the decode step's second launch); MB <= 128.  Like the MFMA path of
+// launch_attention it merges its splits itself.
+hipError_t launch_attention_select(const AttnParams &p, int D, hipStream_t s);
 constexpr int kSelectInAttnMaxMB = 128;
 
 // Split plan of msa_sparse_decode for the given sizes and element types.
 struct AttnPlan {
-    bool mfma;          // per-token MFMA kernel with in-kernel merge (else union VALU + reduce)
+    bool mfma;          // per-token MFMA kernel with in-launch split merge (else union VALU + reduce)
     int32_t splits;
     int32_t bpw;
 };
 AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type);
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k);
 void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                          float **m, float **l, float **acc, int32_t **counters);
+                          float **ml, float **acc, int32_t **counters);
 
 // Launchers return hipSuccess or the launch error; dispatch on element types.
 hipError_t launch_score(const ScoreParams &p, int q_type, int k_type, int Di, hipStream_t s);
