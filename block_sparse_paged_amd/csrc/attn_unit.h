@@ -12,7 +12,7 @@ namespace msa {
 __device__ __forceinline__ int clamp_len(int L, int MB) { return max(0, min(L, MB * kBlock)); }
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kSelSlots = 128;             // per-wave selection slots (k <= MB <= 128)
+constexpr int kSelSlots = 128;             // selection slots (k <= MB <= 128)
 constexpr int kChunk = 32;                 // keys per LDS sub-chunk
 constexpr int kAttnWaves = 8;              // waves per attention workgroup
 constexpr int kWaveKeys = 64;              // keys of a page one wave takes
@@ -84,8 +84,18 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Device-coherent 8-byte accesses (relaxed, agent scope: sc1 loads and stores,
-// no cache-maintenance fences) for the in-launch split hand-off.
+// Device-coherent accesses (agent scope: sc1 loads and stores, no
+// cache-maintenance fences) for the in-launch split hand-off.  The 16-byte
+// forms are inline assembly: a load's result may only be used after an
+// explicit vmcnt wait that names the result register.
+__device__ __forceinline__ void st_coherent4(float *p, f32x4 v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ f32x4 ld_coherent4_nowait(const float *p) {
+    f32x4 v;
+    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
 __device__ __forceinline__ void st_coherent2(float *p, float a, float b) {
     const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
     __hip_atomic_store((uint64_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -117,8 +127,8 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 }
 
 // SEL: the token's selection is computed here from its score row (MB <= 128;
-// every wave redundantly, into its slots) instead of read from topk_idx, and
-// the workgroup of split 0, KV head 0 writes it to topk_idx.
+// by wave 0, into LDS slots) instead of read from topk_idx, and the workgroup
+// of split 0, KV head 0 writes it to topk_idx.
 template <int D, bool SEL>
 __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, const int g, const int qs) {
     constexpr int NW = kAttnWaves;
@@ -137,7 +147,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     __shared__ __attribute__((aligned(16))) uint8_t lk0[NW * CB], lk1[NW * CB];
     __shared__ __attribute__((aligned(16))) uint8_t lv0[NW * CB], lv1[NW * CB];
     __shared__ float smm[NW * 16], sml[NW * 16];
-    __shared__ int sslots[SEL ? NW * kSelSlots : 1];
+    __shared__ int sslots[SEL ? kSelSlots : 1];
     __shared__ int slast;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -186,14 +196,13 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     const int L = clamp_len(Lraw, p.MB);
     const int vis = max(0, L - (p.T - 1 - t));
     if constexpr (SEL) {
-        int *sl = sslots + wave * kSelSlots;
-        select_from_values<2>(srow, p.MB, p.k, sl);
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        __builtin_amdgcn_wave_barrier();
+        // wave 0 selects; the others read its slots
+        if (wave == 0) select_from_values<2>(srow, p.MB, p.k, sslots);
+        __syncthreads();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int idx = lane + 64 * c;
-            tkv[c] = idx < e1 ? sl[idx] : -1;
+            tkv[c] = idx < e1 ? sslots[idx] : -1;
         }
     }
     // nothing but the page loads below may be in the wave's load queue: their
@@ -473,8 +482,8 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     // its stores to complete before the workgroup's single counter increment.
     store_topk();
     if (active) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) st_coherent2(acc_dst + 2 * e, acc8[2 * e], acc8[2 * e + 1]);
+        st_coherent4(acc_dst, f32x4{acc8[0], acc8[1], acc8[2], acc8[3]});
+        st_coherent4(acc_dst + 4, f32x4{acc8[4], acc8[5], acc8[6], acc8[7]});
         if (dq == 0) st_coherent2(ml_dst, mx, lm);
     }
     wait_vmcnt<0>();
@@ -495,19 +504,30 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         for (int e = 0; e < 8; ++e) a2[e] = 0.f;
         for (int s0 = 0; s0 < S; s0 += 4) {
             f32x2 ml[4];
-            float as[4][8];
+            f32x4 alo[4], ahi[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int sp = min(s0 + u, S - 1);
-                ml[u] = ld_coherent2(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
                 const float *src = p.part_acc + part_acc_index(sp, n, h, dq * 8, N, p.Hq, D);
+                alo[u] = ld_coherent4_nowait(src);
+                ahi[u] = ld_coherent4_nowait(src + 4);
+                ml[u] = ld_coherent2(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
+            }
+            // the wait names the loaded registers, so that no use of them is
+            // scheduled before it
+            asm volatile("s_waitcnt vmcnt(0)"
+                         : "+v"(alo[0]), "+v"(alo[1]), "+v"(alo[2]), "+v"(alo[3]), "+v"(ahi[0]),
+                           "+v"(ahi[1]), "+v"(ahi[2]), "+v"(ahi[3])
+                         :
+                         : "memory");
+            float as[4][8];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const f32x2 w = ld_coherent2(src + 2 * e);
-                    as[u][2 * e] = w.x;
-                    as[u][2 * e + 1] = w.y;
+                    as[u][e] = alo[u][e];
+                    as[u][4 + e] = ahi[u][e];
                 }
-            }
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float mu = (s0 + u < S) ? ml[u].x : -INFINITY;

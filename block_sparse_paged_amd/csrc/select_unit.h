@@ -4,9 +4,9 @@
 //
 // Scores become order-preserving unsigned keys (-0 folded onto +0; -inf and
 // NaN become key 0 = not a candidate).  The wave finds the k-th largest key
-// tau bit by bit from the top (tau = the largest x with #{key >= x} >= k),
-// counting with ballots: no LDS and no barrier (it stops early once exactly k
-// keys are >= tau).  Keys above tau are taken, and keys equal to tau in
+// tau two bits at a time from the top (tau = the largest x with
+// #{key >= x} >= k), counting with ballots: no LDS and no barrier (it stops
+// early once exactly k keys are >= tau).  Keys above tau are taken, and keys equal to tau in
 // ascending block id until k are taken, so ties go to the lower id; output positions come from ballot prefix counts, which keeps the
 // ids ascending.  Positions past the candidates get -1.
 #pragma once
@@ -37,21 +37,26 @@ __device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const in
     for (int i = 0; i < KPL; ++i) ncand += __popcll(__ballot(key[i] != 0u));
     const bool take_all = ncand <= k;
 
-    // Once exactly k keys are >= tau, those k are the selection whatever the
-    // lower bits of the k-th key are: the search stops there (the (k+1)-th key
-    // already lies below tau, so no tie crosses the cut).
+    // Two bits of tau per round: the largest of tau|11, tau|10, tau|01 (else
+    // tau|00) that still has >= k keys at or above it (the counts fall as the
+    // trial rises).  Once exactly k keys are >= tau, those k are the selection
+    // whatever the lower bits of the k-th key are: the search stops there (the
+    // (k+1)-th key already lies below tau, so no tie crosses the cut).
     uint32_t tau = 0u;
     if (!take_all) {
 #pragma unroll 1
-        for (int b = 31; b >= 0; --b) {
-            const uint32_t trial = tau | (1u << b);
-            int cnt = 0;
+        for (int b = 30; b >= 0; b -= 2) {
+            const uint32_t t1 = tau | (1u << b), t2 = tau | (2u << b), t3 = tau | (3u << b);
+            int c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
-            for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(key[i] >= trial));
-            if (cnt >= k) {
-                tau = trial;
-                if (cnt == k) break;
+            for (int i = 0; i < KPL; ++i) {
+                c1 += __popcll(__ballot(key[i] >= t1));
+                c2 += __popcll(__ballot(key[i] >= t2));
+                c3 += __popcll(__ballot(key[i] >= t3));
             }
+            const int c = c3 >= k ? c3 : c2 >= k ? c2 : c1 >= k ? c1 : 0;
+            tau = c3 >= k ? t3 : c2 >= k ? t2 : c1 >= k ? t1 : tau;
+            if (c == k) break;
         }
     }
     int above = 0;
