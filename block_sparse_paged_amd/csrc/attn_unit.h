@@ -148,6 +148,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     __shared__ __attribute__((aligned(16))) uint8_t lv0[NW * CB], lv1[NW * CB];
     __shared__ float smm[NW * 16], sml[NW * 16];
     __shared__ int sslots[SEL ? kSelSlots : 1];
+    __shared__ __attribute__((aligned(16))) int shist[SEL ? 256 : 4];
     __shared__ int slast;
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -197,7 +198,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     const int vis = max(0, L - (p.T - 1 - t));
     if constexpr (SEL) {
         // wave 0 selects; the others read its slots
-        if (wave == 0) select_from_values<2>(srow, p.MB, p.k, sslots);
+        if (wave == 0) select_from_values<2>(srow, p.MB, p.k, sslots, shist);
         __syncthreads();
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -400,66 +401,60 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     float l_tot = l_run + __shfl_xor(l_run, 16);
     l_tot += __shfl_xor(l_tot, 32);
 
-    // ---- merge the 8 waves in LDS: o tiles dt < DT/2 in lk0, the rest in lk1,
-    // each as [8 waves][D/2][16 heads] floats
+    // ---- merge the 8 waves in LDS.  Wave w stores tile dt of its O^T
+    // accumulator at [w][dt][lane] (16 bytes per lane: conflict-free vector
+    // accesses), waves 0-3 in lk0 and 4-7 in lk1.  Thread (wm, lane) then
+    // merges tile dt = wm of that lane over the 8 waves: head h0 + lane%16,
+    // d = 16*wm + 4*(lane/16) + 0..3.
     __syncthreads();                                   // every wave's K/V reads done
-    constexpr int DH = D / 2;
-    static_assert(NW * DH * 16 * 4 <= CB * NW, "merge space");
-    float *const mo[2] = {(float *)lk0, (float *)lk1};
+    static_assert(4 * DT * 1024 <= NW * CB, "merge space");
+    {
+        uint8_t *const ow = (wave < 4 ? lk0 : lk1) + (wave & 3) * DT * 1024 + lane * 16;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            mo[dt / (DT / 2)][(wave * DH + (dt % (DT / 2)) * 16 + 4 * grp + e) * 16 + li] = o[dt][e];
+        for (int dt = 0; dt < DT; ++dt) *(f32x4 *)(ow + dt * 1024) = o[dt];
+    }
     if (lane < 16) {
         smm[wave * 16 + lane] = m_run;
         sml[wave * 16 + lane] = l_tot;
     }
     __syncthreads();
-    // thread -> (head hh, 8-wide d group dq); D/8 groups x 16 heads <= 256 of the 512
-    constexpr int DQ = D / 8;
-    const int hh = tid & 15, dq = tid >> 4;
-    const bool active = dq < DQ;
-    const float *mrd = (dq * 8 < DH) ? mo[0] : mo[1];
-    const int dl = (dq * 8) % DH;
+    const int wm = wave;                               // the tile this thread merges
+    const bool active = wm < DT;
     float mw[NW], mx = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) { mw[w] = smm[w * 16 + hh]; mx = fmaxf(mx, mw[w]); }
-    float acc8[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc8[e] = 0.f;
+    for (int w = 0; w < NW; ++w) { mw[w] = smm[w * 16 + li]; mx = fmaxf(mx, mw[w]); }
+    f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
     float lm = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float wgt = exp2_fast(mw[w] - mx);       // -inf -> 0
-            lm += wgt * sml[w * 16 + hh];
-            if (active)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc8[e] += wgt * mrd[(w * DH + dl + e) * 16 + hh];
+            lm += wgt * sml[w * 16 + li];
+            if (active) {
+                const uint8_t *orow = (w < 4 ? lk0 : lk1) + (w & 3) * DT * 1024 + lane * 16;
+                acc4 += wgt * *(const f32x4 *)(orow + wm * 1024);
+            }
         }
     }
-    const int h = h0 + hh;
+    const int h = h0 + li;
+    const int d0 = 16 * wm + 4 * grp;                  // this thread's 4 d
     const int64_t N = (int64_t)p.R * p.T;
-    auto write_out = [&](const float *a, float lsum) {
+    auto write_out = [&](f32x4 a, float lsum) {
         const float inv = (lsum > 0.f) ? p.v_scale / lsum : 0.f;
-        float v[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = lsum > 0.f ? a[e] * inv : 0.f;
-        const int64_t base = n * p.o_sn + (int64_t)h * p.o_sh + (int64_t)(dq * 8) * p.o_sd;
+        const f32x4 v = lsum > 0.f ? a * inv : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t base = n * p.o_sn + (int64_t)h * p.o_sh + (int64_t)d0 * p.o_sd;
         if (p.out_bf16) {
             uint16_t *op = (uint16_t *)p.out;
             if (p.o_sd == 1) {
-                *(uint4 *)(op + base) = make_uint4(cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]),
-                                                   cvt_pk_bf16(v[4], v[5]), cvt_pk_bf16(v[6], v[7]));
+                *(uint2 *)(op + base) = make_uint2(cvt_pk_bf16(v[0], v[1]), cvt_pk_bf16(v[2], v[3]));
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) op[base + e * p.o_sd] = (uint16_t)cvt_pk_bf16(v[e], 0.f);
+                for (int e = 0; e < 4; ++e) op[base + e * p.o_sd] = (uint16_t)cvt_pk_bf16(v[e], 0.f);
             }
         } else {
             float *op = (float *)p.out;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) op[base + e * p.o_sd] = v[e];
+            for (int e = 0; e < 4; ++e) op[base + e * p.o_sd] = v[e];
         }
     };
     auto store_topk = [&]() {
@@ -469,23 +464,20 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         }
     };
     if (p.splits == 1) {
-        if (active) write_out(acc8, lm);
+        if (active) write_out(acc4, lm);
         store_topk();
         return;
     }
     float *const ml_dst = p.part_ml + part_ml_index(qs, n, h, N, p.Hq);
-    float *const acc_dst = p.part_acc + part_acc_index(qs, n, h, dq * 8, N, p.Hq, D);
+    float *const acc_dst = p.part_acc + part_acc_index(qs, n, h, d0, N, p.Hq, D);
     // Split hand-off.  Partials are written and read with device-coherent
     // (sc1) accesses and the arrival counter is a device-scope atomic, so the
     // workgroups of one token may sit on different XCDs; no fence (which would
     // write back and invalidate the whole L2) is needed: each writer waits for
     // its stores to complete before the workgroup's single counter increment.
     store_topk();
-    if (active) {
-        st_coherent4(acc_dst, f32x4{acc8[0], acc8[1], acc8[2], acc8[3]});
-        st_coherent4(acc_dst + 4, f32x4{acc8[4], acc8[5], acc8[6], acc8[7]});
-        if (dq == 0) st_coherent2(ml_dst, mx, lm);
-    }
+    if (active) st_coherent4(acc_dst, acc4);
+    if (wave == 0 && grp == 0) st_coherent2(ml_dst, mx, lm);
     wait_vmcnt<0>();
     __syncthreads();
     int *ctr = p.counters + ((int64_t)n * p.Hkv + g) * kCounterStride;
@@ -499,35 +491,20 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         // every split wrote (m, l, acc) (m = -inf, l = 0, acc = 0 when empty):
         // load them all at once, weight with selects, sum in split order
         const int S = p.splits;
-        float m2 = -INFINITY, l2 = 0.f, a2[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) a2[e] = 0.f;
+        float m2 = -INFINITY, l2 = 0.f;
+        f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
         for (int s0 = 0; s0 < S; s0 += 4) {
             f32x2 ml[4];
-            f32x4 alo[4], ahi[4];
+            f32x4 as[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int sp = min(s0 + u, S - 1);
-                const float *src = p.part_acc + part_acc_index(sp, n, h, dq * 8, N, p.Hq, D);
-                alo[u] = ld_coherent4_nowait(src);
-                ahi[u] = ld_coherent4_nowait(src + 4);
+                as[u] = ld_coherent4_nowait(p.part_acc + part_acc_index(sp, n, h, d0, N, p.Hq, D));
                 ml[u] = ld_coherent2(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
             }
             // the wait names the loaded registers, so that no use of them is
             // scheduled before it
-            asm volatile("s_waitcnt vmcnt(0)"
-                         : "+v"(alo[0]), "+v"(alo[1]), "+v"(alo[2]), "+v"(alo[3]), "+v"(ahi[0]),
-                           "+v"(ahi[1]), "+v"(ahi[2]), "+v"(ahi[3])
-                         :
-                         : "memory");
-            float as[4][8];
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    as[u][e] = alo[u][e];
-                    as[u][4 + e] = ahi[u][e];
-                }
+            asm volatile("s_waitcnt vmcnt(0)" : "+v"(as[0]), "+v"(as[1]), "+v"(as[2]), "+v"(as[3])::"memory");
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const float mu = (s0 + u < S) ? ml[u].x : -INFINITY;
@@ -535,8 +512,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                 const float wo = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
                 const float wn = (mu == -INFINITY) ? 0.f : exp2_fast(mu - mn);
                 l2 = l2 * wo + ml[u].y * wn;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a2[e] = a2[e] * wo + as[u][e] * wn;
+                a2 = a2 * wo + as[u] * wn;
                 m2 = mn;
             }
         }

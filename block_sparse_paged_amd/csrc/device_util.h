@@ -76,6 +76,18 @@ constexpr int kDppXor2 = 0x4E;          // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7-i within 8
 constexpr int kDppMirror = 0x140;       // lane i <-> 15-i within 16
 
+// Inclusive prefix sum over the 64 lanes (lane l gets lanes 0..l): row scans
+// with row_shr (zero fill), then row_bcast15 / row_bcast31 across rows.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+    return x;
+}
+
 // Sum over aligned groups of W lanes (W power of two, <= 64); every lane of a
 // group ends with the group sum.
 template <int W>

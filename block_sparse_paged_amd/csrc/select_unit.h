@@ -3,12 +3,13 @@
 // token's blocks from the score row itself).
 //
 // Scores become order-preserving unsigned keys (-0 folded onto +0; -inf and
-// NaN become key 0 = not a candidate).  The wave finds the k-th largest key
-// tau two bits at a time from the top (tau = the largest x with
-// #{key >= x} >= k), counting with ballots: no LDS and no barrier (it stops
-// early once exactly k keys are >= tau).  Keys above tau are taken, and keys equal to tau in
-// ascending block id until k are taken, so ties go to the lower id; output positions come from ballot prefix counts, which keeps the
-// ids ascending.  Positions past the candidates get -1.
+// NaN become key 0 = not a candidate).  The k-th largest key tau is found by a
+// radix select over the bytes of the keys (LDS histograms, see
+// kth_largest_key); keys above tau are taken, and keys equal to tau in
+// ascending block id until k are taken, so ties go to the lower id; output
+// positions come from ballot prefix counts, which keeps the ids ascending.
+// Positions past the candidates get -1.  Integer work only: exact and
+// deterministic.
 #pragma once
 
 #include "device_util.h"
@@ -27,38 +28,60 @@ __device__ __forceinline__ int lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// The k-th largest candidate key (key 0 excluded; there are more than k
+// candidates), found one byte at a time from the top: each pass counts the
+// candidates that match the bytes found so far into a 256-bin histogram in
+// LDS (hist: 256 ints owned by the wave), and the bin holding the
+// need-th largest of them gives the next byte.  It stops early when that
+// bin's keys are exactly the ones still needed; the value returned then has
+// the remaining bytes zero, and exactly k keys are >= it.
+template <int KPL>
+__device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&key)[KPL], const int k, int *hist) {
+    const int lane = threadIdx.x & 63;
+    uint32_t prefix = 0u, pmask = 0u;
+    int need = k;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        *(int4 *)(hist + 4 * lane) = make_int4(0, 0, 0, 0);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+        for (int i = 0; i < KPL; ++i)
+            if (key[i] != 0u && (key[i] & pmask) == prefix)
+                __hip_atomic_fetch_add(hist + ((key[i] >> shift) & 255u), 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WAVEFRONT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // lane l holds bins 255-4l (h.w) down to 252-4l (h.x)
+        const int4 h = *(const int4 *)(hist + 252 - 4 * lane);
+        const int t = h.x + h.y + h.z + h.w;
+        const int above_lane = wave_prefix_sum(t) - t;         // candidates in bins > 255-4l
+        // S(b): candidates in bins >= b
+        const int sa = above_lane + h.w, sb = sa + h.z, sc = sb + h.y, sd = sc + h.x;
+        const uint64_t m = __ballot(sd >= need);               // nonzero: lane 63 counts all
+        const int L = __builtin_ctzll(m);                      // lane of the top bin with S >= need
+        const int jj = sa >= need ? 0 : sb >= need ? 1 : sc >= need ? 2 : 3;
+        const int sj = jj == 0 ? sa : jj == 1 ? sb : jj == 2 ? sc : sd;
+        const int hj = jj == 0 ? h.w : jj == 1 ? h.z : jj == 2 ? h.y : h.x;
+        const int bin = 255 - 4 * L - __builtin_amdgcn_readlane(jj, L);
+        const int s_bin = __builtin_amdgcn_readlane(sj, L), h_bin = __builtin_amdgcn_readlane(hj, L);
+        need -= s_bin - h_bin;                                 // the keys in higher bins are taken
+        prefix |= (uint32_t)bin << shift;
+        pmask |= 255u << shift;
+        if (h_bin == need) break;                              // all of this bin is taken
+    }
+    return prefix;
+}
+
 // key[i] of lane l is the key of block i*64 + l (0 past MB).  emit(pos, id) is
-// called for pos in [0, k): the selected ids ascending, then -1.
+// called for pos in [0, k): the selected ids ascending, then -1.  hist: 256
+// ints of LDS owned by the wave.
 template <int KPL, class Emit>
-__device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const int k, Emit emit) {
+__device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const int k, int *hist, Emit emit) {
     const int lane = threadIdx.x & 63;
     int ncand = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) ncand += __popcll(__ballot(key[i] != 0u));
     const bool take_all = ncand <= k;
-
-    // Two bits of tau per round: the largest of tau|11, tau|10, tau|01 (else
-    // tau|00) that still has >= k keys at or above it (the counts fall as the
-    // trial rises).  Once exactly k keys are >= tau, those k are the selection
-    // whatever the lower bits of the k-th key are: the search stops there (the
-    // (k+1)-th key already lies below tau, so no tie crosses the cut).
-    uint32_t tau = 0u;
-    if (!take_all) {
-#pragma unroll 1
-        for (int b = 30; b >= 0; b -= 2) {
-            const uint32_t t1 = tau | (1u << b), t2 = tau | (2u << b), t3 = tau | (3u << b);
-            int c1 = 0, c2 = 0, c3 = 0;
-#pragma unroll
-            for (int i = 0; i < KPL; ++i) {
-                c1 += __popcll(__ballot(key[i] >= t1));
-                c2 += __popcll(__ballot(key[i] >= t2));
-                c3 += __popcll(__ballot(key[i] >= t3));
-            }
-            const int c = c3 >= k ? c3 : c2 >= k ? c2 : c1 >= k ? c1 : 0;
-            tau = c3 >= k ? t3 : c2 >= k ? t2 : c1 >= k ? t1 : tau;
-            if (c == k) break;
-        }
-    }
+    const uint32_t tau = take_all ? 0u : kth_largest_key<KPL>(key, k, hist);
     int above = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) above += __popcll(__ballot(key[i] > tau));
@@ -80,7 +103,7 @@ __device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const in
 
 // Score row n of the sheet -> topk row n.
 template <int KPL>
-__device__ __forceinline__ void select_row(const TopkParams &p, const int64_t n) {
+__device__ __forceinline__ void select_row(const TopkParams &p, const int64_t n, int *hist) {
     const int lane = threadIdx.x & 63;
     uint32_t key[KPL];
 #pragma unroll
@@ -89,19 +112,19 @@ __device__ __forceinline__ void select_row(const TopkParams &p, const int64_t n)
         key[i] = id < p.MB ? score_key(p.scores[n * p.sc_sn + (int64_t)id * p.sc_sj]) : 0u;
     }
     int32_t *dst = p.topk + n * p.tk_sn;
-    select_keys<KPL>(key, p.k, [&](int pos, int id) { dst[(int64_t)pos * p.tk_si] = id; });
+    select_keys<KPL>(key, p.k, hist, [&](int pos, int id) { dst[(int64_t)pos * p.tk_si] = id; });
 }
 
 // Scores already in registers (v[i] of lane l = score of block i*64 + l) ->
 // slots[0..k) (LDS).
 template <int KPL>
 __device__ __forceinline__ void select_from_values(const float (&v)[KPL], const int MB, const int k,
-                                                   int *slots) {
+                                                   int *slots, int *hist) {
     const int lane = threadIdx.x & 63;
     uint32_t key[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) key[i] = (i * 64 + lane < MB) ? score_key(v[i]) : 0u;
-    select_keys<KPL>(key, k, [&](int pos, int id) { slots[pos] = id; });
+    select_keys<KPL>(key, k, hist, [&](int pos, int id) { slots[pos] = id; });
 }
 
 }  // namespace msa

@@ -17,9 +17,11 @@ namespace {
 
 template <int KPL>
 __global__ __launch_bounds__(256) void topk_kernel(TopkParams p) {
-    const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    __shared__ __attribute__((aligned(16))) int hist[4][256];
+    const int wave = threadIdx.x >> 6;
+    const int64_t n = (int64_t)blockIdx.x * 4 + wave;
     if (n >= p.N) return;
-    select_row<KPL>(p, n);
+    select_row<KPL>(p, n, hist[wave]);
 }
 
 template <int KPL>
