@@ -51,6 +51,15 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernels", default="score,select,decode,select_decode,calls",
                     help="extra timing graphs to build (per call, and the three-call step)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run a plain fp32 streaming kernel (out = in * 1) over this many MiB, "
+                         "8 times, as the reference for HBM byte counters")
+    ap.add_argument("--calib-out", default=os.path.join(ROOT, "gpurun_out"),
+                    help="directory for calib.json (the copy size and the calls' algorithmic bytes)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script made with --calib-copy-mib, write profiles/traffic.json, print a "
+                         "table; needs no GPU")
     return ap.parse_args()
 
 
@@ -88,6 +97,59 @@ def algorithmic_bytes(case, topk: np.ndarray) -> dict:
                 step=score + select_decode, calls=score + select + attend, index=index, kv=kv)
 
 
+# kernels whose counters the PMC summary reports, by the call that launches them
+PMC_KERNELS = {"select_decode": "attn_token_select_kernel", "score": "score_mfma_decode_kernel"}
+CALIB_KERNEL = "MulFunctor"          # the reference streaming kernel of --calib-copy-mib
+
+
+def pmc_means(run_dir: str, counter: str) -> dict:
+    """Mean value of `counter` per dispatch for each kernel name in a rocprofv3 CSV run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        for row in csv.DictReader(open(f)):
+            if row["Counter_Name"] != counter:
+                continue
+            vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def pmc_summary(fetch_dir: str, write_dir: str) -> None:
+    """HBM traffic per launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each
+    scaled by what the counter reads for the reference copy of known size."""
+    fetch, write = pmc_means(fetch_dir, "FETCH_SIZE"), pmc_means(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        hits = [v for k, v in d.items() if key in k]
+        if not hits:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+        return sum(hits) / len(hits)
+
+    meta = json.load(open(os.path.join(fetch_dir, "calib.json")))
+    copy_bytes = meta["copy_bytes"]
+    f_factor = pick(fetch, CALIB_KERNEL) * 1024 / copy_bytes
+    w_factor = pick(write, CALIB_KERNEL) * 1024 / copy_bytes
+    calls, raw = {}, {}
+    for call, key in PMC_KERNELS.items():
+        fk, wk = pick(fetch, key), pick(write, key)
+        raw[call] = {"FETCH_SIZE_KiB": round(fk, 1), "WRITE_SIZE_KiB": round(wk, 1)}
+        calls[call] = int(fk * 1024 / f_factor + wk * 1024 / w_factor)
+    out = {"source_digest": kernel_source_digest(), "copy_bytes": copy_bytes,
+           "fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+           "calls": calls, "raw": raw, "algorithmic_bytes": meta.get("algorithmic_bytes")}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(f"reference copy: {copy_bytes} B read + written; FETCH_SIZE reads {f_factor:.3f} x the "
+          f"bytes, WRITE_SIZE {w_factor:.3f} x\n")
+    print("| call (kernel) | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (calibrated) | algorithmic bytes |")
+    print("|---|---|---|---|---|")
+    for call, key in PMC_KERNELS.items():
+        alg = (meta.get("algorithmic_bytes") or {}).get(call)
+        print(f"| {call} (`{key}`) | {raw[call]['FETCH_SIZE_KiB']} | {raw[call]['WRITE_SIZE_KiB']} | "
+              f"{calls[call]} | {alg} |")
+
+
 def cpu_baseline(case, min_wall: float = 1.0) -> dict:
     """The oracle's full step on the host cores, repeated for at least min_wall s."""
     import oracle
@@ -113,6 +175,9 @@ def cpu_baseline(case, min_wall: float = 1.0) -> dict:
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported "
               "(the sharded path is described, not built)", file=sys.stderr)
@@ -159,6 +224,14 @@ def main():
                                   case.k_scale, case.v_scale, case.B, ws[i])
 
     stream = torch.cuda.Stream()
+    if a.calib_copy_mib > 0:
+        n = a.calib_copy_mib << 18                      # fp32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(M):
@@ -252,6 +325,12 @@ def main():
                      "algorithmic_bytes": ab[dom],
                      "duration_us": round(t_dom * 1e6, 3) if t_dom else None},
     }
+    if a.calib_copy_mib > 0:
+        # the reference copy's size and the calls' algorithmic bytes, for --pmc-summary
+        os.makedirs(a.calib_out, exist_ok=True)
+        with open(os.path.join(a.calib_out, "calib.json"), "w") as fh:
+            json.dump({"copy_bytes": a.calib_copy_mib << 20,
+                       "algorithmic_bytes": {c: ab[c] for c in PMC_KERNELS}}, fh)
     if not a.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(case)
     print(json.dumps(res), flush=True)
