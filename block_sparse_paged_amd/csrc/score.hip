@@ -184,8 +184,20 @@ template <int DI>
 __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
     const int wave = threadIdx.x >> 6;
     const int JC = (p.MB + 3) >> 2;
-    const int r = blockIdx.x / JC;
-    const int j = (blockIdx.x % JC) * 4 + wave;
+    int r, jc;
+    if (p.R >= 8) {
+        // workgroup b runs on XCD b % 8: the row's workgroups all go to XCD r % 8,
+        // where the attention workgroups of its tokens run (block table and
+        // score row stay in that XCD's L2)
+        const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+        r = x + 8 * (i / JC);
+        jc = i % JC;
+        if (r >= p.R) return;
+    } else {
+        r = blockIdx.x / JC;
+        jc = blockIdx.x % JC;
+    }
+    const int j = jc * 4 + wave;
     if (j >= p.MB) return;                      // no barriers in this kernel
     score_page<DI>(p, r, j);
 }
@@ -354,7 +366,9 @@ hipError_t launch_valu(const ScoreParams &p, hipStream_t s) {
 
 template <int DI>
 hipError_t launch_mfma_decode(const ScoreParams &p, hipStream_t s) {
-    const int64_t grid = (int64_t)p.R * ((p.MB + 3) / 4);
+    const int64_t JC = (p.MB + 3) / 4;
+    // R >= 8: 8 XCDs x ceil(R / 8) rows each x JC (see the kernel)
+    const int64_t grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * JC : (int64_t)p.R * JC;
     hipLaunchKernelGGL((score_mfma_decode_kernel<DI>), dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
