@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--k", type=int, default=16)
     ap.add_argument("--copies", type=int, default=8, help="pool copies rotated per graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill block-score measurement")
     ap.add_argument("--kernels", default="score,select,decode,select_decode,calls",
                     help="extra timing graphs to build (per call, and the three-call step)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -148,6 +150,58 @@ def pmc_summary(fetch_dir: str, write_dir: str) -> None:
         alg = (meta.get("algorithmic_bytes") or {}).get(call)
         print(f"| {call} (`{key}`) | {raw[call]['FETCH_SIZE_KiB']} | {raw[call]['WRITE_SIZE_KiB']} | "
               f"{calls[call]} | {alg} |")
+
+
+def prefill_score(torch, msa, synth, copies: int = 4, reps: int = 50) -> dict:
+    """The prefill variant of the block score (4 rows x 2048 new tokens over an
+    8192-token prefix, FP8 index, Di = 128), an MFMA-bound contraction, and the
+    top-k over its [8192, 80] sheet, each timed alone like the decode calls."""
+    c = synth.prefill()
+    dev = "cuda"
+    q_idx, bt, sl = c.q_idx.to(dev), c.block_table.to(dev), c.seq_lens.to(dev)
+    idx0 = c.index_k.view(torch.float8_e4m3fn).to(dev)
+    pools = [idx0] + [idx0.clone() for _ in range(copies - 1)]
+    scores = [torch.full((c.N, c.MB), float("nan"), device=dev) for _ in range(copies)]
+    topk = [torch.full((c.N, c.k), -1, dtype=torch.int32, device=dev) for _ in range(copies)]
+    stream = torch.cuda.Stream()
+
+    def graph(fn):
+        with torch.cuda.stream(stream):
+            for i in range(copies):
+                fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(copies):
+                fn(i)
+        with torch.cuda.stream(stream):
+            for _ in range(5):
+                g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1000.0 / (reps * copies)
+
+    t_score = graph(lambda i: msa.msa_block_score(q_idx, pools[i], bt, sl, c.T, c.B, c.idx_scale,
+                                                  scores[i]))
+    t_sel = graph(lambda i: msa.msa_select_topk(scores[i], c.k, topk[i]))
+    lens = c.seq_lens.numpy().astype(np.int64)
+    # dot products over the visible keys: token t of a row sees L - (T - 1 - t) keys
+    dots = int(sum(int(L) * c.T - c.T * (c.T - 1) // 2 for L in lens))
+    flops = 2 * dots * c.Di
+    tflops = flops / t_score / 1e12
+    return {"workload": "prefill block score: 4 rows x 2048 new tokens over an 8192-token prefix "
+                        "(seq_len 10240, 80 blocks), FP8 index, Di=128, top-k 16 over [8192, 80]",
+            "score_us": round(t_score * 1e6, 3), "select_us": round(t_sel * 1e6, 3),
+            "algorithmic_gflop": round(flops / 1e9, 3),
+            "roofline": {"bound": "mfma", "kernel": "score_prefill_kernel<128, 8>", "achieved": round(tflops, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
 def cpu_baseline(case, min_wall: float = 1.0) -> dict:
@@ -325,6 +379,8 @@ def main():
                      "algorithmic_bytes": ab[dom],
                      "duration_us": round(t_dom * 1e6, 3) if t_dom else None},
     }
+    if not a.no_prefill:
+        res["prefill_score"] = prefill_score(torch, msa, synth)
     if a.calib_copy_mib > 0:
         # the reference copy's size and the calls' algorithmic bytes, for --pmc-summary
         os.makedirs(a.calib_out, exist_ok=True)

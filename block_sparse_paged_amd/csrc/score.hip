@@ -203,155 +203,240 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
 }
 
 // ------------------------------------------------------------------ MFMA path
+//
+// Prefill rows (T > 16): a GEMM per row, S = Q_r K_r^T over the row's visible
+// keys, reduced to block maxima.  A workgroup of 4 waves owns 64*QT query
+// tokens of a row (16*QT per wave = QT MFMA column tiles of 16) and a chunk of
+// PC consecutive blocks; the tiles are laid out so that the workgroups of one
+// query chunk run on one XCD.  The chunk's live pages stream through a 3-deep
+// ring of LDS buffers with direct-to-LDS loads (each wave issues a quarter of
+// every page; explicit vmcnt waits, one barrier per page), two pages ahead of
+// the math.  The query rows are read coalesced and transposed into the MFMA
+// operand layout through LDS.  Per 16-key tile and k-step a lane reads 8 FP8
+// bytes of its key row from LDS, decodes them to bf16 once and feeds them to
+// QT MFMAs: at QT = 8 the decode and the running max cost one VALU
+// instruction per MFMA, a quarter of its issue time.  Pages that every token
+// sees whole skip the causal mask.  The running block max per (query, block)
+// is staged in LDS and written out coalesced at the end.
 
-constexpr int kMQ = 128;      // query tokens per workgroup (4 waves x 2 tiles x 16)
-constexpr int kMBlocks = 8;   // blocks per workgroup
+constexpr int kPMaxPC = 8;        // blocks per workgroup, at most
+constexpr int kPTargetWGs = 512;  // workgroups aimed for (two per CU)
 
-// LDS page layout: [128 keys][DI bytes] FP8, 8-byte units XOR-swizzled by key so
-// that the 16 lanes reading one MFMA fragment column hit distinct banks.
-template <int DI>
-__device__ __forceinline__ int page_off(int key, int unit) {
-    constexpr int UNITS = DI / 8;
-    return key * DI + ((unit ^ (key & (UNITS - 1))) << 3);
+// max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
+// first, unlike fmaxf); the operands are dot products, never NaN (a NaN dot
+// product is outside the contract)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-template <int DI>
-__global__ __launch_bounds__(256) void score_mfma_kernel(ScoreParams p) {
-    constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
-    constexpr int PAGE = kBlock * DI;           // bytes per page
-    constexpr int CHUNKS = PAGE / 16;           // 16-byte chunks per page
-    constexpr int PER_T = CHUNKS / 256;         // chunks per thread
-    static_assert(PER_T >= 1, "page too small");
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][PAGE];
+// S^T tile for keys 16*kt .. +15 of the page in `buf` against the wave's QT
+// query tiles: acc[qt][e] = q . k for key 16*kt + 4*grp + e and query column
+// lane%16.  K-step ks covers d = 32*ks .. +31, lane group grp its d = 32*ks +
+// 8*grp .. +7 (an 8-byte LDS read of FP8 codes, decoded to bf16 once for the
+// QT MFMAs that use it).
+template <int DI, int QT>
+__device__ __forceinline__ void prefill_tile(const uint8_t *buf, int kt, int li, int grp,
+                                             const uint4 (&qf)[QT][DI / 32], f32x4 (&acc)[QT]) {
+    constexpr int KS = DI / 32, CPR = DI / 16;
+    const int key = kt * 16 + li;
+    const uint8_t *krow = buf + key * DI + (grp & 1) * 8;
+    const int ksw = key & (CPR - 1) & 7;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int unit = 2 * ks + (grp >> 1);
+        const uint2 raw = *(const uint2 *)(krow + ((unit ^ ksw) << 4));
+        uint4 a;
+        a.x = fp8x2_to_bf16x2<false>(raw.x); a.y = fp8x2_to_bf16x2<true>(raw.x);
+        a.z = fp8x2_to_bf16x2<false>(raw.y); a.w = fp8x2_to_bf16x2<true>(raw.y);
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            acc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
+    }
+}
 
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int QC = (p.T + kMQ - 1) / kMQ;
-    const int BC = (p.MB + kMBlocks - 1) / kMBlocks;
-    int bid = blockIdx.x;
-    const int bc = bid % BC;
-    bid /= BC;
-    const int qc = bid % QC;
-    const int r = bid / QC;
+template <int DI, int QT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void score_prefill_kernel(ScoreParams p, int PC) {
+    constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
+    constexpr int CPR = DI / 16;                // 16-byte units per key row
+    constexpr int KPL = 64 / CPR;               // keys per 1 KiB direct-to-LDS load
+    constexpr int LPP = kBlock / KPL;           // loads per page
+    constexpr int LPW = LPP / 4;                // loads per page per wave
+    constexpr int PAGE = kBlock * DI;
+    constexpr int PQ = 64 * QT;                 // query tokens per workgroup
+    static_assert(LPW >= 1 && KPL % 8 == 0, "page layout");
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[3][PAGE];
+    __shared__ float sbuf[PQ][kPMaxPC + 1];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+    const int QC = (p.T + PQ - 1) / PQ;
+    const int NPC = (p.MB + PC - 1) / PC;
+    // Tiles u = (r*QC + qc)*NPC + pc.  Workgroups are dispatched round-robin
+    // over the 8 XCDs (XCD = blockIdx % 8), each with its own L2; XCD x runs
+    // the contiguous tile range [x*U8, (x+1)*U8), so the workgroups of one
+    // query chunk (and of one row's pages) share an L2 instead of every XCD
+    // fetching every chunk.
+    const int U = p.R * QC * NPC, U8 = (U + 7) / 8;
+    int u = (int)(blockIdx.x % 8) * U8 + (int)(blockIdx.x / 8);
+    if (u >= U) return;                                    // whole workgroup, before any barrier
+    const int pc = u % NPC;
+    u /= NPC;
+    const int qc = u % QC;
+    const int r = u / QC;
     const int L = clamp_len(p.seq_lens[(int64_t)r * p.sl_s], p.MB);
-    const int tq0 = qc * kMQ;                          // first token of the WG (in row)
-    const int tq1 = min(p.T, tq0 + kMQ);               // one past the last
-    const int vmax_wg = max(0, L - (p.T - 1 - (tq1 - 1)));
-    const int j0 = bc * kMBlocks;
-    const int j1 = min(p.MB, j0 + kMBlocks);
+    const int tq0 = qc * PQ, tq1 = min(p.T, tq0 + PQ);
+    const int vmin = max(0, L - (p.T - 1 - tq0));        // keys seen by the WG's first token
+    const int vmax = max(0, L - (p.T - 1 - (tq1 - 1)));  // ... by its last
+    const int j0 = pc * PC, npg = min(p.MB, j0 + PC) - j0;
     const int64_t nrow = (int64_t)r * p.T;
 
-    // B-operand fragments of Q^T: for tile qt, k-step ks, lane holds
-    // q_idx[token 16*qt + lane%16][d = 32*ks + 8*(lane/16) .. +8] (bf16).
-    // vt[qt]: keys visible to that token.
-    uint4 qf[2][KS];
-    int vt[2];
+    // page table of the chunk: lane i holds block j0 + i (npg <= 8 < 64)
+    const int pid_l = lane < npg ? p.bt[(int64_t)r * p.bt_sr + (int64_t)(j0 + lane) * p.bt_sj] : -1;
+
+    const bool vis_l = lane < npg && (j0 + lane) * kBlock < vmax;
+    const bool ok_l = pid_l >= 0 && pid_l < p.P;
+    const uint64_t live = __ballot(vis_l && ok_l);
+    const int key0 = lane / CPR, slot = lane % CPR;
+    auto issue = [&](int pi, int b) {                      // this wave's quarter of page pi
+        const int pid = __builtin_amdgcn_readlane(pid_l, pi);
+        const uint8_t *pg = (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp +
+                            (int64_t)key0 * p.k_sb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-        const int t = tq0 + wave * 32 + qt * 16 + (lane & 15);
-        vt[qt] = (t < p.T) ? max(0, L - (p.T - 1 - t)) : 0;
+        for (int l = 0; l < LPW; ++l) {
+            const int ld = wave * LPW + l;
+            dma16_nt(pg + (int64_t)(ld * KPL) * p.k_sb, kbuf[b] + ld * 1024);
+        }
+    };
+    // The first two live pages go out before the query rows: a wave's LDS
+    // reads issued while its own direct-to-LDS loads are outstanding were
+    // measured to stall the transpose below by far more than the loads'
+    // latency, and with the pages issued first, the waits for the query rows
+    // (younger loads, in-order counter) imply the pages have landed.
+    uint64_t todo = live;
+    int q0 = -1, q1 = -1;                                  // the two pages in flight
+    if (todo) { q0 = __builtin_ctzll(todo); todo &= todo - 1; issue(q0, 0); }
+    if (todo) { q1 = __builtin_ctzll(todo); todo &= todo - 1; issue(q1, 1); }
+
+    // Query rows, read coalesced.  In the MFMA operand layout consecutive
+    // lanes hold different query rows, and a global load in that layout
+    // touches a separate cache line for every lane of a 4-lane quad, several
+    // times slower than quads reading 64 contiguous bytes.  So each wave reads
+    // its 16*QT rows with whole rows across consecutive lanes and transposes
+    // them through 16 rows' worth of LDS of its own (below).  Columns past
+    // the row's last token read that token again; their scores are never
+    // stored, and no reduction mixes columns.
+    constexpr int UPR = DI / 8;                 // 16-byte units per bf16 query row
+    constexpr int RPL = 64 / UPR;               // rows per coalesced load
+    constexpr int LPT = 16 / RPL;               // loads per 16-row tile
+    uint4 qraw[QT][LPT];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (t < p.T) {
-                const uint16_t *q = (const uint16_t *)p.q_idx + (nrow + t) * p.q_sn;
-                qf[qt][ks] = *(const uint4 *)(q + 32 * ks + 8 * (lane >> 4));
-            } else {
-                qf[qt][ks] = make_uint4(0, 0, 0, 0);
-            }
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int l = 0; l < LPT; ++l) {
+            const int t = min(p.T - 1, tq0 + 16 * QT * wave + 16 * qt + l * RPL + lane / UPR);
+            qraw[qt][l] = *(const uint4 *)((const uint16_t *)p.q_idx + (nrow + t) * p.q_sn + 8 * (lane % UPR));
+        }
+
+    // blocks without a live page: -inf for tokens that see none of their keys,
+    // NaN for tokens that see keys of a block whose page id is out of range
+    for (int idx = tid; idx < PQ * npg; idx += 256) {
+        const int qq = idx / npg, pi = idx % npg;
+        if (!((live >> pi) & 1)) {
+            const int v = max(0, L - (p.T - 1 - (tq0 + qq)));
+            const int pid = __shfl(pid_l, pi);
+            const bool bad = (j0 + pi) * kBlock < v && !(pid >= 0 && pid < p.P);
+            sbuf[qq][pi] = bad ? __builtin_nanf("") : -INFINITY;
         }
     }
 
-    auto page_ptr = [&](int j) -> const uint8_t * {
-        const int pid = p.bt[(int64_t)r * p.bt_sr + (int64_t)j * p.bt_sj];
-        return (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp;
-    };
-    auto page_ok = [&](int j) -> int {
-        if (j * kBlock >= vmax_wg) return 0;                 // nothing visible in the WG
-        const int pid = p.bt[(int64_t)r * p.bt_sr + (int64_t)j * p.bt_sj];
-        return (pid >= 0 && pid < p.P) ? 1 : 2;               // 2 = bad page id
-    };
-
-    uint4 stage[PER_T];
-    auto load_page = [&](int j) {
-        const uint8_t *pg = page_ptr(j);
+    // B operand of S^T = K Q^T: for tile qt and k-step ks the lane holds query
+    // tq0 + 16*QT*wave + 16*qt + lane%16 at d = 32*ks + 8*(lane/16) .. +7.
+    // The transpose goes through the third page buffer, which no page load
+    // uses before the loop's first barrier; each wave owns 16 rows of it, 16-
+    // byte units XOR-swizzled by row so that neither side has bank conflicts.
+    // LDS accesses of one wave complete in order, so no barrier is needed.
+    static_assert(4 * 16 * DI * 2 <= PAGE, "transpose area");
+    uint8_t *const stage = kbuf[2] + wave * (16 * DI * 2);
+    uint4 qf[QT][KS];
+    int vt[QT];
 #pragma unroll
-        for (int c = 0; c < PER_T; ++c) {
-            const int chunk = tid + 256 * c;
-            const int key = chunk / (DI / 16);
-            const int col = (chunk % (DI / 16)) * 16;
-            stage[c] = *(const uint4 *)(pg + (int64_t)key * p.k_sb + col);
-        }
-    };
-    auto store_page = [&](int buf) {
+    for (int qt = 0; qt < QT; ++qt) {
+        const int t = tq0 + 16 * QT * wave + 16 * qt + li;
+        vt[qt] = (t < p.T) ? max(0, L - (p.T - 1 - t)) : 0;
 #pragma unroll
-        for (int c = 0; c < PER_T; ++c) {
-            const int chunk = tid + 256 * c;
-            const int key = chunk / (DI / 16);
-            const int unit = (chunk % (DI / 16)) * 2;
-            *(uint2 *)&lds[buf][page_off<DI>(key, unit)] = make_uint2(stage[c].x, stage[c].y);
-            *(uint2 *)&lds[buf][page_off<DI>(key, unit + 1)] = make_uint2(stage[c].z, stage[c].w);
+        for (int l = 0; l < LPT; ++l) {
+            const int row = l * RPL + lane / UPR, unit = lane % UPR;
+            *(uint4 *)(stage + row * (DI * 2) + ((unit ^ (row & (UPR - 1))) << 4)) = qraw[qt][l];
         }
-    };
-
-    // find the next block (from j) whose page must be read
-    int jn = j0;
-    while (jn < j1 && page_ok(jn) != 1) ++jn;
-    if (jn < j1) load_page(jn);
-    int buf = 0;
-    for (int j = j0; j < j1; ++j) {
-        const int ok = page_ok(j);                             // uniform over the WG
-        if (ok != 1) {
-            const float v = ok == 0 ? -INFINITY : __builtin_nanf("");
-            for (int t = tid; t < tq1 - tq0; t += 256)
-                p.scores[(nrow + tq0 + t) * p.sc_sn + (int64_t)j * p.sc_sj] = v;
-            continue;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int unit = 4 * ks + grp;
+            qf[qt][ks] = *(const uint4 *)(stage + li * (DI * 2) + ((unit ^ (li & (UPR - 1))) << 4));
         }
-        store_page(buf);
-        __syncthreads();
-        jn = j + 1;
-        while (jn < j1 && page_ok(jn) != 1) ++jn;
-        if (jn < j1) load_page(jn);                            // overlaps the MFMAs below
+    }
+    // the first two pages, the query fragments and the table reads above have
+    // all landed before the loop, whose waits count positions in the wave's
+    // load queue
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-        const int kbase = j * kBlock;
-        float best[2] = {-INFINITY, -INFINITY};
+    const float scale = p.idx_scale;
+    for (int i = 0; q0 >= 0; ++i) {
+        const int b = i % 3;
+        if (q1 >= 0) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();                                   // page q0 complete; buffer (i+2)%3 free
+        int q2 = -1;
+        if (todo) { q2 = __builtin_ctzll(todo); todo &= todo - 1; issue(q2, (i + 2) % 3); }
+        const int kbase = (j0 + q0) * kBlock;
+        const uint8_t *buf = kbuf[b];
+        float best[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) best[qt] = -INFINITY;
+        if (kbase + kBlock <= vmin) {                      // every key visible to every token
 #pragma unroll 2
-        for (int kt = 0; kt < 8; ++kt) {
-            // A operand: K rows (keys) 16*kt + lane%16, d = 32*ks + 8*(lane/16) .. +8
-            f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            const int key = kt * 16 + (lane & 15);
+            for (int kt = 0; kt < 8; ++kt) {
+                f32x4 acc[QT];
+                prefill_tile<DI, QT>(buf, kt, li, grp, qf, acc);
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const uint2 raw = *(const uint2 *)&lds[buf][page_off<DI>(key, ks * 4 + (lane >> 4))];
-                uint4 kb;
-                kb.x = fp8x2_to_bf16x2<false>(raw.x);
-                kb.y = fp8x2_to_bf16x2<true>(raw.x);
-                kb.z = fp8x2_to_bf16x2<false>(raw.y);
-                kb.w = fp8x2_to_bf16x2<true>(raw.y);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, kb);
-#pragma unroll
-                for (int qt = 0; qt < 2; ++qt)
-                    acc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        a, __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
-            }
-            // acc[qt][i] = S^T[key 16*kt + 4*(lane/16) + i][token lane%16]
-#pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int pos = kbase + kt * 16 + 4 * (lane >> 4) + i;
-                    best[qt] = (pos < vt[qt]) ? fmaxf(best[qt], acc[qt][i]) : best[qt];
+                for (int qt = 0; qt < QT; ++qt) {
+                    best[qt] = max3f(best[qt], acc[qt][0], acc[qt][1]);
+                    best[qt] = max3f(best[qt], acc[qt][2], acc[qt][3]);
                 }
-        }
-        // combine the four lane groups (lane/16) that hold keys of the same token
+            }
+        } else {                                           // causal edge: mask key >= V(token)
+            int lim[QT];
 #pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-            const float v = max_across_groups<16>(best[qt]);
-            const int t = tq0 + wave * 32 + qt * 16 + (lane & 15);
-            if (lane < 16 && t < p.T)
-                p.scores[(nrow + t) * p.sc_sn + (int64_t)j * p.sc_sj] = v * p.idx_scale;
+            for (int qt = 0; qt < QT; ++qt) lim[qt] = vt[qt] - kbase - 4 * grp;
+            for (int kt = 0; kt < 8; ++kt) {
+                f32x4 acc[QT];
+                prefill_tile<DI, QT>(buf, kt, li, grp, qf, acc);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    float m[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m[e] = (kt * 16 + e < lim[qt]) ? acc[qt][e] : -INFINITY;
+                    best[qt] = max3f(best[qt], m[0], m[1]);
+                    best[qt] = max3f(best[qt], m[2], m[3]);
+                }
+            }
         }
-        buf ^= 1;
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const float v = max_across_groups<16>(best[qt]);
+            if (grp == 0) sbuf[16 * QT * wave + 16 * qt + li][q0] = v * scale;
+        }
+        q0 = q1;
+        q1 = q2;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < (tq1 - tq0) * npg; idx += 256) {
+        const int qq = idx / npg, pi = idx % npg;
+        p.scores[(nrow + tq0 + qq) * p.sc_sn + (int64_t)(j0 + pi) * p.sc_sj] = sbuf[qq][pi];
     }
 }
 
@@ -373,13 +458,22 @@ hipError_t launch_mfma_decode(const ScoreParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DI, int QT>
+hipError_t launch_prefill(const ScoreParams &p, hipStream_t s) {
+    const int64_t QC = (p.T + 64 * QT - 1) / (64 * QT);
+    int64_t PC = ((int64_t)p.MB * p.R * QC + kPTargetWGs - 1) / kPTargetWGs;
+    PC = PC < 1 ? 1 : (PC > kPMaxPC ? kPMaxPC : PC);
+    const int64_t U = (int64_t)p.R * QC * ((p.MB + PC - 1) / PC);
+    const int64_t grid = 8 * ((U + 7) / 8);               // tile ranges per XCD (see the kernel)
+    if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;   // the kernel indexes tiles in int
+    hipLaunchKernelGGL((score_prefill_kernel<DI, QT>), dim3((unsigned)grid), dim3(256), 0, s, p, (int)PC);
+    return hipGetLastError();
+}
+
+// 8 query tiles per wave once a row has more than 256 query tokens, else 4
 template <int DI>
 hipError_t launch_mfma(const ScoreParams &p, hipStream_t s) {
-    const int QC = (p.T + kMQ - 1) / kMQ;
-    const int BC = (p.MB + kMBlocks - 1) / kMBlocks;
-    const int64_t grid = (int64_t)p.R * QC * BC;
-    hipLaunchKernelGGL((score_mfma_kernel<DI>), dim3((unsigned)grid), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return p.T > 256 ? launch_prefill<DI, 8>(p, s) : launch_prefill<DI, 4>(p, s);
 }
 
 template <bool QB, bool KF>

@@ -140,6 +140,8 @@ SMALL = [
     dict(R=2, T=2, lens=(2000, 2500), k=5, shared_pages=True, P=40),
     dict(R=2, T=40, lens=(300, 1700), k=4),          # MFMA score path, ragged
     dict(R=1, T=130, lens=(1200,), k=3, D=64, Di=64),
+    dict(R=2, T=300, lens=(400, 2000), k=4, D=64, Di=64),   # 8 query tiles per wave
+    dict(R=2, T=600, lens=(700, 1900), k=5),        # two 512-token query chunks, ragged
     dict(R=2, T=4, lens=(600, 900), k=4, Hq=32),     # 2 KV heads via Hkv below
 ]
 
