@@ -205,22 +205,27 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
 // ------------------------------------------------------------------ MFMA path
 //
 // Prefill rows (T > 16): a GEMM per row, S = Q_r K_r^T over the row's visible
-// keys, reduced to block maxima.  A workgroup of 4 waves owns 64*QT query
-// tokens of a row (16*QT per wave = QT MFMA column tiles of 16) and a chunk of
-// PC consecutive blocks; the tiles are laid out so that the workgroups of one
-// query chunk run on one XCD.  The chunk's live pages stream through a 3-deep
-// ring of LDS buffers with direct-to-LDS loads (each wave issues a quarter of
-// every page; explicit vmcnt waits, one barrier per page), two pages ahead of
-// the math.  The query rows are read coalesced and transposed into the MFMA
-// operand layout through LDS.  Per 16-key tile and k-step a lane reads 8 FP8
-// bytes of its key row from LDS, decodes them to bf16 once and feeds them to
-// QT MFMAs: at QT = 8 the decode and the running max cost one VALU
-// instruction per MFMA, a quarter of its issue time.  Pages that every token
-// sees whole skip the causal mask.  The running block max per (query, block)
-// is staged in LDS and written out coalesced at the end.
+// keys, reduced to block maxima.  A workgroup of 8 waves (two per SIMD, one
+// workgroup per CU) owns 128*QT query tokens of a row (16*QT per wave = QT
+// MFMA column tiles of 16) and an even share of the blocks those tokens see
+// (at most kPMaxPC consecutive ones); the tiles are laid out so that the
+// workgroups of one query chunk run on one XCD.  The query rows are read
+// coalesced and transposed into the MFMA operand layout through LDS.
+//
+// Each live page is read once per workgroup with coalesced 16-byte loads
+// (every thread a 32-byte slice of a key row), decoded FP8 -> bf16 once and
+// stored to one of two bf16 page buffers in LDS, from which all 8 waves read
+// their A operands ready to use: the decode costs 16 VALU instructions per
+// wave and page instead of one per MFMA, and VALU issue does not overlap MFMA
+// issue well on a SIMD.  The next page's slice is loaded into registers while
+// the current page is multiplied, decoded and stored after it (one barrier
+// per page).  Pages that every token sees whole skip the causal mask.  The
+// running block max per (query, block) is staged in LDS and written out
+// coalesced at the end.
 
+constexpr int kPWaves = 8;        // waves per workgroup, two per SIMD
 constexpr int kPMaxPC = 8;        // blocks per workgroup, at most
-constexpr int kPTargetWGs = 512;  // workgroups aimed for (two per CU)
+constexpr int kPTargetWGs = 256;  // workgroups aimed for (one per CU)
 
 // max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
 // first, unlike fmaxf); the operands are dot products, never NaN (a NaN dot
@@ -229,98 +234,116 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// S^T tile for keys 16*kt .. +15 of the page in `buf` against the wave's QT
-// query tiles: acc[qt][e] = q . k for key 16*kt + 4*grp + e and query column
-// lane%16.  K-step ks covers d = 32*ks .. +31, lane group grp its d = 32*ks +
-// 8*grp .. +7 (an 8-byte LDS read of FP8 codes, decoded to bf16 once for the
-// QT MFMAs that use it).
+// S^T tile for keys 16*kt .. +15 of the bf16 page in `buf` against the
+// wave's QT query tiles: acc[qt][e] = q . k for key 16*kt + 4*grp + e and
+// query column lane%16.  K-step ks covers d = 32*ks .. +31, lane group grp
+// its d = 32*ks + 8*grp .. +7: 16-byte unit 4*ks + grp of the key's bf16 row,
+// stored XOR-swizzled by the key.
 template <int DI, int QT>
 __device__ __forceinline__ void prefill_tile(const uint8_t *buf, int kt, int li, int grp,
                                              const uint4 (&qf)[QT][DI / 32], f32x4 (&acc)[QT]) {
-    constexpr int KS = DI / 32, CPR = DI / 16;
+    constexpr int KS = DI / 32, UPR = DI / 8;
     const int key = kt * 16 + li;
-    const uint8_t *krow = buf + key * DI + (grp & 1) * 8;
-    const int ksw = key & (CPR - 1) & 7;
+    const uint8_t *krow = buf + key * (DI * 2);
+    uint4 a[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *(const uint4 *)(krow + (((4 * ks + grp) ^ (key & (UPR - 1))) << 4));
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int unit = 2 * ks + (grp >> 1);
-        const uint2 raw = *(const uint2 *)(krow + ((unit ^ ksw) << 4));
-        uint4 a;
-        a.x = fp8x2_to_bf16x2<false>(raw.x); a.y = fp8x2_to_bf16x2<true>(raw.x);
-        a.z = fp8x2_to_bf16x2<false>(raw.y); a.w = fp8x2_to_bf16x2<true>(raw.y);
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt)
             acc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
-    }
+                __builtin_bit_cast(bf16x8, a[ks]), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
 }
 
 template <int DI, int QT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void score_prefill_kernel(ScoreParams p, int PC) {
+__global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void score_prefill_kernel(ScoreParams p, int WPC) {
     constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
-    constexpr int CPR = DI / 16;                // 16-byte units per key row
-    constexpr int KPL = 64 / CPR;               // keys per 1 KiB direct-to-LDS load
-    constexpr int LPP = kBlock / KPL;           // loads per page
-    constexpr int LPW = LPP / 4;                // loads per page per wave
-    constexpr int PAGE = kBlock * DI;
-    constexpr int PQ = 64 * QT;                 // query tokens per workgroup
-    static_assert(LPW >= 1 && KPL % 8 == 0, "page layout");
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf[3][PAGE];
+    constexpr int NT = 64 * kPWaves;            // threads per workgroup
+    constexpr int PQ = 16 * QT * kPWaves;       // query tokens per workgroup
+    constexpr int RB = DI * 2;                  // bytes per bf16 row (query or key)
+    constexpr int UPR = DI / 8;                 // 16-byte units per bf16 row
+    constexpr int VPT = kBlock * DI / (16 * NT) > 0 ? kBlock * DI / (16 * NT) : 1;  // 16-byte FP8 loads per slice
+    constexpr int TPK = DI / (16 * VPT);        // slices per key row
+    constexpr int NLD = TPK * kBlock;           // threads holding a slice (whole waves)
+    static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
+    __shared__ __attribute__((aligned(16))) uint8_t kb[2][kBlock * RB];
     __shared__ float sbuf[PQ][kPMaxPC + 1];
+    static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the page buffers");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int grp = lane >> 4, li = lane & 15;
     const int QC = (p.T + PQ - 1) / PQ;
-    const int NPC = (p.MB + PC - 1) / PC;
-    // Tiles u = (r*QC + qc)*NPC + pc.  Workgroups are dispatched round-robin
-    // over the 8 XCDs (XCD = blockIdx % 8), each with its own L2; XCD x runs
-    // the contiguous tile range [x*U8, (x+1)*U8), so the workgroups of one
-    // query chunk (and of one row's pages) share an L2 instead of every XCD
-    // fetching every chunk.
-    const int U = p.R * QC * NPC, U8 = (U + 7) / 8;
-    int u = (int)(blockIdx.x % 8) * U8 + (int)(blockIdx.x / 8);
+    // Query chunk c = r*QC + qc has WPC workgroups, tiles u = c*WPC + w.
+    // Workgroups are dispatched round-robin over the 8 XCDs (XCD = blockIdx %
+    // 8), each with its own L2; XCD x runs the contiguous tile range [x*U8,
+    // (x+1)*U8), so the workgroups of one query chunk (and of one row's pages)
+    // share an L2 instead of every XCD fetching every chunk.
+    const int U = p.R * QC * WPC, U8 = (U + 7) / 8;
+    const int u = (int)(blockIdx.x % 8) * U8 + (int)(blockIdx.x / 8);
     if (u >= U) return;                                    // whole workgroup, before any barrier
-    const int pc = u % NPC;
-    u /= NPC;
-    const int qc = u % QC;
-    const int r = u / QC;
+    const int c = u / WPC, qc = c % QC, r = c / QC, w = u % WPC;
     const int L = clamp_len(p.seq_lens[(int64_t)r * p.sl_s], p.MB);
     const int tq0 = qc * PQ, tq1 = min(p.T, tq0 + PQ);
     const int vmin = max(0, L - (p.T - 1 - tq0));        // keys seen by the WG's first token
     const int vmax = max(0, L - (p.T - 1 - (tq1 - 1)));  // ... by its last
-    const int j0 = pc * PC, npg = min(p.MB, j0 + PC) - j0;
     const int64_t nrow = (int64_t)r * p.T;
+    // Blocks the chunk's last token sees: 0 .. lp-1.  They are split evenly
+    // over the chunk's workgroups (at most kPMaxPC each, by the choice of
+    // WPC); blocks from lp on are seen by no token of the chunk: -inf, written
+    // by workgroup w for every WPC-th of them.
+    const int lp = min(p.MB, (vmax + kBlock - 1) / kBlock);
+    const int j0 = (int)((int64_t)w * lp / WPC), npg = (int)((int64_t)(w + 1) * lp / WPC) - j0;
+    for (int jd = lp + w; jd < p.MB; jd += WPC)
+        for (int qq = tid; qq < tq1 - tq0; qq += NT)
+            p.scores[(nrow + tq0 + qq) * p.sc_sn + (int64_t)jd * p.sc_sj] = -INFINITY;
 
-    // page table of the chunk: lane i holds block j0 + i (npg <= 8 < 64)
+    // page table of the share: lane i holds block j0 + i (npg <= 8 < 64)
     const int pid_l = lane < npg ? p.bt[(int64_t)r * p.bt_sr + (int64_t)(j0 + lane) * p.bt_sj] : -1;
-
     const bool vis_l = lane < npg && (j0 + lane) * kBlock < vmax;
     const bool ok_l = pid_l >= 0 && pid_l < p.P;
-    const uint64_t live = __ballot(vis_l && ok_l);
-    const int key0 = lane / CPR, slot = lane % CPR;
-    auto issue = [&](int pi, int b) {                      // this wave's quarter of page pi
+    uint64_t todo = __ballot(vis_l && ok_l);               // live pages, in block order
+    auto next_live = [&]() {
+        if (!todo) return -1;
+        const int pi = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        return pi;
+    };
+    // this thread's slice of a page (threads below NLD): key tid / TPK, bytes
+    // 16*VPT*(tid % TPK) ..
+    const int skey = tid / TPK, spart = tid % TPK;
+    uint4 pv[VPT];
+    auto load_page = [&](int pi) {
+        if (NLD < NT && tid >= NLD) return;
         const int pid = __builtin_amdgcn_readlane(pid_l, pi);
-        const uint8_t *pg = (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp +
-                            (int64_t)key0 * p.k_sb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
+        const uint8_t *src = (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp + (int64_t)skey * p.k_sb +
+                             16 * VPT * spart;
 #pragma unroll
-        for (int l = 0; l < LPW; ++l) {
-            const int ld = wave * LPW + l;
-            dma16_nt(pg + (int64_t)(ld * KPL) * p.k_sb, kbuf[b] + ld * 1024);
+        for (int h = 0; h < VPT; ++h) pv[h] = *(const uint4 *)(src + 16 * h);
+    };
+    auto store_page = [&](uint8_t *dst) {                  // decode the slice to bf16 into dst
+        if (NLD < NT && tid >= NLD) return;
+        uint8_t *row = dst + skey * RB;
+#pragma unroll
+        for (int h = 0; h < VPT; ++h) {
+            const int u0 = 2 * (VPT * spart + h);          // bf16 unit of the slice's first 8 codes
+            uint4 lo, hi;
+            lo.x = fp8x2_to_bf16x2<false>(pv[h].x); lo.y = fp8x2_to_bf16x2<true>(pv[h].x);
+            lo.z = fp8x2_to_bf16x2<false>(pv[h].y); lo.w = fp8x2_to_bf16x2<true>(pv[h].y);
+            hi.x = fp8x2_to_bf16x2<false>(pv[h].z); hi.y = fp8x2_to_bf16x2<true>(pv[h].z);
+            hi.z = fp8x2_to_bf16x2<false>(pv[h].w); hi.w = fp8x2_to_bf16x2<true>(pv[h].w);
+            *(uint4 *)(row + ((u0 ^ (skey & (UPR - 1))) << 4)) = lo;
+            *(uint4 *)(row + (((u0 + 1) ^ (skey & (UPR - 1))) << 4)) = hi;
         }
     };
-    // The first two live pages go out before the query rows: a wave's LDS
-    // reads issued while its own direct-to-LDS loads are outstanding were
-    // measured to stall the transpose below by far more than the loads'
-    // latency, and with the pages issued first, the waits for the query rows
-    // (younger loads, in-order counter) imply the pages have landed.
-    uint64_t todo = live;
-    int q0 = -1, q1 = -1;                                  // the two pages in flight
-    if (todo) { q0 = __builtin_ctzll(todo); todo &= todo - 1; issue(q0, 0); }
-    if (todo) { q1 = __builtin_ctzll(todo); todo &= todo - 1; issue(q1, 1); }
+    int cur = next_live();
+    // The first page is requested before the query rows: the other order was
+    // measured to be far slower.
+    if (cur >= 0) load_page(cur);
 
     // Query rows, read coalesced.  In the MFMA operand layout consecutive
     // lanes hold different query rows, and a global load in that layout
@@ -330,7 +353,6 @@ void score_prefill_kernel(ScoreParams p, int PC) {
     // them through 16 rows' worth of LDS of its own (below).  Columns past
     // the row's last token read that token again; their scores are never
     // stored, and no reduction mixes columns.
-    constexpr int UPR = DI / 8;                 // 16-byte units per bf16 query row
     constexpr int RPL = 64 / UPR;               // rows per coalesced load
     constexpr int LPT = 16 / RPL;               // loads per 16-row tile
     uint4 qraw[QT][LPT];
@@ -344,7 +366,8 @@ void score_prefill_kernel(ScoreParams p, int PC) {
 
     // blocks without a live page: -inf for tokens that see none of their keys,
     // NaN for tokens that see keys of a block whose page id is out of range
-    for (int idx = tid; idx < PQ * npg; idx += 256) {
+    const uint64_t live = __ballot(vis_l && ok_l);
+    for (int idx = tid; idx < PQ * npg; idx += NT) {
         const int qq = idx / npg, pi = idx % npg;
         if (!((live >> pi) & 1)) {
             const int v = max(0, L - (p.T - 1 - (tq0 + qq)));
@@ -356,12 +379,11 @@ void score_prefill_kernel(ScoreParams p, int PC) {
 
     // B operand of S^T = K Q^T: for tile qt and k-step ks the lane holds query
     // tq0 + 16*QT*wave + 16*qt + lane%16 at d = 32*ks + 8*(lane/16) .. +7.
-    // The transpose goes through the third page buffer, which no page load
-    // uses before the loop's first barrier; each wave owns 16 rows of it, 16-
-    // byte units XOR-swizzled by row so that neither side has bank conflicts.
-    // LDS accesses of one wave complete in order, so no barrier is needed.
-    static_assert(4 * 16 * DI * 2 <= PAGE, "transpose area");
-    uint8_t *const stage = kbuf[2] + wave * (16 * DI * 2);
+    // Each wave transposes through 16 rows of LDS of its own (inside the page
+    // buffers, before any page is stored there), 16-byte units XOR-swizzled
+    // by row so that neither side has bank conflicts.  LDS accesses of one
+    // wave complete in order, so the wave needs no barrier of its own.
+    uint8_t *const stage = &kb[0][0] + wave * (16 * RB);
     uint4 qf[QT][KS];
     int vt[QT];
 #pragma unroll
@@ -371,41 +393,43 @@ void score_prefill_kernel(ScoreParams p, int PC) {
 #pragma unroll
         for (int l = 0; l < LPT; ++l) {
             const int row = l * RPL + lane / UPR, unit = lane % UPR;
-            *(uint4 *)(stage + row * (DI * 2) + ((unit ^ (row & (UPR - 1))) << 4)) = qraw[qt][l];
+            *(uint4 *)(stage + row * RB + ((unit ^ (row & (UPR - 1))) << 4)) = qraw[qt][l];
         }
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int unit = 4 * ks + grp;
-            qf[qt][ks] = *(const uint4 *)(stage + li * (DI * 2) + ((unit ^ (li & (UPR - 1))) << 4));
+            qf[qt][ks] = *(const uint4 *)(stage + li * RB + ((unit ^ (li & (UPR - 1))) << 4));
         }
     }
-    // the first two pages, the query fragments and the table reads above have
-    // all landed before the loop, whose waits count positions in the wave's
-    // load queue
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    // first live page to LDS (once every wave is done with its transpose
+    // area); the second one's slice on its way
+    __syncthreads();
+    if (cur >= 0) store_page(kb[0]);
+    int nxt = next_live();
+    if (nxt >= 0) load_page(nxt);
+    __syncthreads();
 
     const float scale = p.idx_scale;
-    for (int i = 0; q0 >= 0; ++i) {
-        const int b = i % 3;
-        if (q1 >= 0) wait_vmcnt<LPW>();
-        else wait_vmcnt<0>();
-        __syncthreads();                                   // page q0 complete; buffer (i+2)%3 free
-        int q2 = -1;
-        if (todo) { q2 = __builtin_ctzll(todo); todo &= todo - 1; issue(q2, (i + 2) % 3); }
-        const int kbase = (j0 + q0) * kBlock;
-        const uint8_t *buf = kbuf[b];
+    for (int i = 0; cur >= 0; ++i) {
+        const int kbase = (j0 + cur) * kBlock;
+        const uint8_t *buf = kb[i & 1];
         float best[QT];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) best[qt] = -INFINITY;
         if (kbase + kBlock <= vmin) {                      // every key visible to every token
-#pragma unroll 2
-            for (int kt = 0; kt < 8; ++kt) {
-                f32x4 acc[QT];
-                prefill_tile<DI, QT>(buf, kt, li, grp, qf, acc);
+            // the max of tile kt is taken after tile kt+1's MFMAs are issued,
+            // so that it runs while they execute instead of waiting for kt's
+            f32x4 acc[2][QT];
+            prefill_tile<DI, QT>(buf, 0, li, grp, qf, acc[0]);
+#pragma unroll
+            for (int kt = 1; kt <= 8; ++kt) {
+                if (kt < 8) prefill_tile<DI, QT>(buf, kt, li, grp, qf, acc[kt & 1]);
+                const f32x4 *done = acc[(kt - 1) & 1];
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) {
-                    best[qt] = max3f(best[qt], acc[qt][0], acc[qt][1]);
-                    best[qt] = max3f(best[qt], acc[qt][2], acc[qt][3]);
+                    best[qt] = max3f(best[qt], done[qt][0], done[qt][1]);
+                    best[qt] = max3f(best[qt], done[qt][2], done[qt][3]);
                 }
             }
         } else {                                           // causal edge: mask key >= V(token)
@@ -428,13 +452,18 @@ void score_prefill_kernel(ScoreParams p, int PC) {
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const float v = max_across_groups<16>(best[qt]);
-            if (grp == 0) sbuf[16 * QT * wave + 16 * qt + li][q0] = v * scale;
+            if (grp == 0) sbuf[16 * QT * wave + 16 * qt + li][cur] = v * scale;
         }
-        q0 = q1;
-        q1 = q2;
+        // the other buffer held the previous page, done by every wave before
+        // the last barrier
+        if (nxt >= 0) store_page(kb[(i + 1) & 1]);
+        const int after = next_live();
+        if (after >= 0) load_page(after);
+        __syncthreads();
+        cur = nxt;
+        nxt = after;
     }
-    __syncthreads();
-    for (int idx = tid; idx < (tq1 - tq0) * npg; idx += 256) {
+    for (int idx = tid; idx < (tq1 - tq0) * npg; idx += NT) {
         const int qq = idx / npg, pi = idx % npg;
         p.scores[(nrow + tq0 + qq) * p.sc_sn + (int64_t)(j0 + pi) * p.sc_sj] = sbuf[qq][pi];
     }
@@ -460,20 +489,24 @@ hipError_t launch_mfma_decode(const ScoreParams &p, hipStream_t s) {
 
 template <int DI, int QT>
 hipError_t launch_prefill(const ScoreParams &p, hipStream_t s) {
-    const int64_t QC = (p.T + 64 * QT - 1) / (64 * QT);
-    int64_t PC = ((int64_t)p.MB * p.R * QC + kPTargetWGs - 1) / kPTargetWGs;
-    PC = PC < 1 ? 1 : (PC > kPMaxPC ? kPMaxPC : PC);
-    const int64_t U = (int64_t)p.R * QC * ((p.MB + PC - 1) / PC);
+    const int64_t QC = (p.T + 16 * QT * kPWaves - 1) / (16 * QT * kPWaves), chunks = (int64_t)p.R * QC;
+    // workgroups per query chunk: enough for kPTargetWGs in all, and enough
+    // that none holds more than kPMaxPC blocks; no more than there are blocks
+    int64_t WPC = (kPTargetWGs + chunks - 1) / chunks;
+    WPC = WPC < (p.MB + kPMaxPC - 1) / kPMaxPC ? (p.MB + kPMaxPC - 1) / kPMaxPC : WPC;
+    WPC = WPC > p.MB ? p.MB : WPC;
+    const int64_t U = chunks * WPC;
     const int64_t grid = 8 * ((U + 7) / 8);               // tile ranges per XCD (see the kernel)
     if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;   // the kernel indexes tiles in int
-    hipLaunchKernelGGL((score_prefill_kernel<DI, QT>), dim3((unsigned)grid), dim3(256), 0, s, p, (int)PC);
+    hipLaunchKernelGGL((score_prefill_kernel<DI, QT>), dim3((unsigned)grid), dim3(64 * kPWaves), 0, s, p, (int)WPC);
     return hipGetLastError();
 }
 
-// 8 query tiles per wave once a row has more than 256 query tokens, else 4
+// 4 query tiles per wave (512 tokens per workgroup) once a row has more than
+// 256 query tokens, else 2
 template <int DI>
 hipError_t launch_mfma(const ScoreParams &p, hipStream_t s) {
-    return p.T > 256 ? launch_prefill<DI, 8>(p, s) : launch_prefill<DI, 4>(p, s);
+    return p.T > 256 ? launch_prefill<DI, 4>(p, s) : launch_prefill<DI, 2>(p, s);
 }
 
 template <bool QB, bool KF>
