@@ -199,7 +199,7 @@ def prefill_score(torch, msa, synth, copies: int = 4, reps: int = 50) -> dict:
                         "(seq_len 10240, 80 blocks), FP8 index, Di=128, top-k 16 over [8192, 80]",
             "score_us": round(t_score * 1e6, 3), "select_us": round(t_sel * 1e6, 3),
             "algorithmic_gflop": round(flops / 1e9, 3),
-            "roofline": {"bound": "mfma", "kernel": "score_prefill_kernel<128, 8>", "achieved": round(tflops, 1),
+            "roofline": {"bound": "mfma", "kernel": "score_prefill_kernel<128, 4>", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
