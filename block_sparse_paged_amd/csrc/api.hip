@@ -188,11 +188,13 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     desc(c, q, 3);
     desc(c, k_cache, 4);
     desc(c, v_cache, 4);
-    desc(c, topk_idx, 2);
+    // [N, k] shared by the KV heads, or [Hkv, N, k] one selection per KV head
+    const bool per_head = topk_idx && topk_idx->ndim == 3;
+    desc(c, topk_idx, per_head ? 3 : 2);
     desc(c, out, 3);
     paging(c, block_table, seq_lens);
     dtype_in(c, q, {MSA_BF16, MSA_F32});
-    dtype_in(c, k_cache, {MSA_FP8_E4M3FN, MSA_F32});
+    dtype_in(c, k_cache, {MSA_FP8_E4M3FN, MSA_BF16, MSA_F32});
     dtype_in(c, topk_idx, {MSA_I32});
     dtype_in(c, out, {MSA_BF16, MSA_F32});
     if (!c.ok()) return c.err;
@@ -205,8 +207,9 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     const int64_t Hq = q->shape[1];
     D = (int)q->shape[2];
     const int64_t P = k_cache->shape[0], Hkv = k_cache->shape[2];
-    const int64_t K = topk_idx->shape[1];
-    if (q->shape[0] != N || topk_idx->shape[0] != N) c.fail(MSA_ERR_SHAPE);
+    const int64_t K = topk_idx->shape[per_head ? 2 : 1];
+    if (q->shape[0] != N || topk_idx->shape[per_head ? 1 : 0] != N) c.fail(MSA_ERR_SHAPE);
+    if (per_head && topk_idx->shape[0] != Hkv) c.fail(MSA_ERR_SHAPE);
     if (k_cache->shape[1] != kBlock || k_cache->shape[3] != D) c.fail(MSA_ERR_SHAPE);
     for (int i = 0; i < 4; ++i)
         if (v_cache->shape[i] != k_cache->shape[i]) c.fail(MSA_ERR_SHAPE);
@@ -231,7 +234,10 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     p.bt = (const int32_t *)block_table->data;
     p.bt_sr = block_table->stride[0]; p.bt_sj = block_table->stride[1];
     p.seq_lens = (const int32_t *)seq_lens->data; p.sl_s = seq_lens->stride[0];
-    p.topk = (const int32_t *)topk_idx->data; p.tk_sn = topk_idx->stride[0]; p.tk_si = topk_idx->stride[1];
+    p.topk = (const int32_t *)topk_idx->data;
+    p.tk_sg = per_head ? topk_idx->stride[0] : 0;
+    p.tk_sn = topk_idx->stride[per_head ? 1 : 0];
+    p.tk_si = topk_idx->stride[per_head ? 2 : 1];
     p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
     p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
     plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kvt);

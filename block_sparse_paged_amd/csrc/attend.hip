@@ -75,7 +75,7 @@ __device__ int build_union(const AttnParams &p, const Group &q, uint32_t (*sel)[
     const int64_t n0 = (int64_t)q.r * p.T + q.t0;
     for (int e = tid; e < q.nt * p.k; e += 256) {
         const int t = e / p.k, i = e - t * p.k;
-        const int j = p.topk[(n0 + t) * p.tk_sn + (int64_t)i * p.tk_si];
+        const int j = p.topk[(int64_t)q.g * p.tk_sg + (n0 + t) * p.tk_sn + (int64_t)i * p.tk_si];
         if (j < 0 || j >= p.MB || j * kBlock >= token_vis(p, q, t)) continue;
         const int pid = p.bt[(int64_t)q.r * p.bt_sr + (int64_t)j * p.bt_sj];
         if (pid < 0 || pid >= p.P) continue;
@@ -173,17 +173,20 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_token_select_kernel(A
 
 // ------------------------------------------------------------------ VALU path
 
-template <bool QBF16, bool KVFP8>
+// one K/V element of type KVT (E_FP8 code, bf16 or f32) as float (exact)
+template <int KVT>
 __device__ __forceinline__ float load_elem(const void *base, int64_t i) {
-    if constexpr (KVFP8) {
+    if constexpr (KVT == E_FP8) {
         const uint8_t c = ((const uint8_t *)base)[i];
         return fp8x2_to_f32x2<false>((uint32_t)c).x;
+    } else if constexpr (KVT == E_BF16) {
+        return __uint_as_float((uint32_t)((const uint16_t *)base)[i] << 16);
     } else {
         return ((const float *)base)[i];
     }
 }
 
-template <bool QBF16, bool KVFP8, int D>
+template <bool QBF16, int KVT, int D>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     constexpr int DPL = D / 64;                    // output dims per lane
     constexpr int GMAX = 16;
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
                 float dot = 0.f;
                 if (key < nk) {
                     for (int d = 0; d < D; ++d)
-                        dot = fmaf(qs[w][d], load_elem<QBF16, KVFP8>(p.k_cache, kpage + key * p.k_sb + d), dot);
+                        dot = fmaf(qs[w][d], load_elem<KVT>(p.k_cache, kpage + key * p.k_sb + d), dot);
                     lg[e] = dot * scale2;
                 } else {
                     lg[e] = -INFINITY;
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
                 const int d = lane + 64 * e;
                 float a = st_acc[w][hh][d] * alpha;
                 for (int key = 0; key < nk; ++key)
-                    a = fmaf(pbuf[w][key], load_elem<QBF16, KVFP8>(p.v_cache, vpage + key * p.v_sb + d), a);
+                    a = fmaf(pbuf[w][key], load_elem<KVT>(p.v_cache, vpage + key * p.v_sb + d), a);
                 st_acc[w][hh][d] = a;
             }
             if (lane == 0) {
@@ -379,19 +382,21 @@ hipError_t launch_token_select(const AttnParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool QB, bool KF, int D>
+template <bool QB, int KVT, int D>
 hipError_t launch_valu(const AttnParams &p, int64_t grid, hipStream_t s) {
-    hipLaunchKernelGGL((attn_valu_kernel<QB, KF, D>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_valu_kernel<QB, KVT, D>), dim3((unsigned)grid), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_valu_types(const AttnParams &p, int qt, int kt, int64_t grid, hipStream_t s) {
-    const bool qb = qt == E_BF16, kf = kt == E_FP8;
-    if (qb && kf) return launch_valu<true, true, D>(p, grid, s);
-    if (qb) return launch_valu<true, false, D>(p, grid, s);
-    if (kf) return launch_valu<false, true, D>(p, grid, s);
-    return launch_valu<false, false, D>(p, grid, s);
+    const bool qb = qt == E_BF16;
+    switch (kt) {
+    case E_FP8: return qb ? launch_valu<true, E_FP8, D>(p, grid, s) : launch_valu<false, E_FP8, D>(p, grid, s);
+    case E_BF16: return qb ? launch_valu<true, E_BF16, D>(p, grid, s) : launch_valu<false, E_BF16, D>(p, grid, s);
+    case E_F32: return qb ? launch_valu<true, E_F32, D>(p, grid, s) : launch_valu<false, E_F32, D>(p, grid, s);
+    }
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -454,7 +459,7 @@ void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hk
 }
 
 bool attention_supported(int q_type, int kv_type, int D, int G) {
-    if (!((q_type == E_F32 || q_type == E_BF16) && (kv_type == E_F32 || kv_type == E_FP8)))
+    if (!((q_type == E_F32 || q_type == E_BF16) && (kv_type == E_F32 || kv_type == E_BF16 || kv_type == E_FP8)))
         return false;
     if (!(D == 64 || D == 128)) return false;
     return G >= 1 && G <= 16;

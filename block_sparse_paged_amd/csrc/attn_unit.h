@@ -163,7 +163,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     // One round trip for the small inputs: seq_len, the selection row up to e1
     // (lane l holds entries l + 64c) or the score row, the row's block table
     // (lane l holds logical blocks l and l + 64) and the query fragments.
-    const int64_t trow = (int64_t)n * p.tk_sn;
+    const int64_t trow = (int64_t)g * p.tk_sg + (int64_t)n * p.tk_sn;
     int tkv[4];
     float srow[2];
     if constexpr (SEL) {

@@ -36,7 +36,7 @@ struct AttnParams {
     const void *v_cache; int64_t v_sp, v_sb, v_sh;
     const int32_t *bt;   int64_t bt_sr, bt_sj;
     const int32_t *seq_lens; int64_t sl_s;
-    const int32_t *topk; int64_t tk_sn, tk_si;     // [N, k]
+    const int32_t *topk; int64_t tk_sg, tk_sn, tk_si;  // [Hkv, N, k]; tk_sg = 0: [N, k] shared
     // selection computed in the attention kernel: score sheet in, topk out
     const float *scores; int64_t sc_sn, sc_sj;     // [N, MB]
     int32_t *topk_out;                             // same strides as topk

@@ -144,10 +144,14 @@ size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
  * is skipped; duplicate ids in one row count once.
  *
  *   q           [N, Hq, D]      bf16 | f32      innermost stride 1
- *   k_cache     [P, B, Hkv, D]  fp8e4m3fn | f32 innermost stride 1, 16-byte aligned rows
+ *   k_cache     [P, B, Hkv, D]  fp8e4m3fn | bf16 | f32   innermost stride 1, 16-byte
+ *                               aligned rows (bf16: the dense cache of attention.decode)
  *   v_cache     [P, B, Hkv, D]  same dtype and shape as k_cache
  *   block_table [R, MB] i32, seq_lens [R] i32   as for msa_block_score
- *   topk_idx    [N, k]          i32             any strides; shared by all KV heads
+ *   topk_idx    [N, k] i32, shared by all KV heads, or [Hkv, N, k] i32, one
+ *               selection per KV head (attention.decode's (Hkv, B, K) layout:
+ *               query head h attends the blocks of topk_idx[h / (Hq/Hkv)]);
+ *               any strides
  *   tokens_per_row  T >= 1
  *   out         [N, Hq, D]      bf16 | f32 OUT  any strides
  *   sm_scale, k_scale, v_scale  finite floats
@@ -160,7 +164,8 @@ size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
  *               not run concurrently.
  * D must be 64 or 128.  When Hq/Hkv == 16 with bf16 queries and FP8 caches the
  * QK^T and PV products run on bf16 MFMA tiles (FP8 decoded exactly, P rounded
- * to bf16); otherwise on vector ALUs in fp32.
+ * to bf16); otherwise (bf16 or f32 caches, other head ratios) on vector ALUs
+ * in fp32.
  */
 void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
                        const msa_tensor *v_cache, const msa_tensor *block_table,
@@ -180,6 +185,7 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
  * stores topk_idx; otherwise the top-k kernel runs first.
  *
  *   scores      [N, MB] f32, N = R * tokens_per_row, MB = block_table's width
+ *   topk_idx    [N, k] i32 OUT (one selection for all KV heads: one index head)
  *   workspace   as for msa_sparse_decode (same size query, same contract)
  */
 void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,

@@ -149,14 +149,33 @@ def select_topk(scores, k: int) -> np.ndarray:
 def sparse_decode(q, k_cache, v_cache, block_table, seq_lens, topk_idx, T: int,
                   sm_scale: float, k_scale: float, v_scale: float,
                   n_range: Optional[tuple[int, int]] = None, threads: int = 1) -> np.ndarray:
-    """out [N, Hq, D] float64 (rows outside ``n_range`` are NaN)."""
+    """out [N, Hq, D] float64 (rows outside ``n_range`` are NaN).
+
+    ``topk_idx`` is [N, K] (one selection shared by every KV head) or [Hkv, N, K]
+    (one selection per KV head, the (Hkv, B, K) layout of attention.decode in
+    Cacheon "Kernel ABI", "Attention block slots"): query head h attends the
+    blocks of topk_idx[h // (Hq // Hkv)].  The per-head form is the shared form
+    evaluated once per KV head, keeping that head's query heads."""
+    tk_all = np.asarray(torch.as_tensor(topk_idx, dtype=torch.int32).cpu())
+    if tk_all.ndim == 3:
+        Hkv, Hq = k_cache.shape[2], q.shape[1]
+        assert tk_all.shape[0] == Hkv and Hq % Hkv == 0
+        G = Hq // Hkv
+        out = None
+        for g in range(Hkv):
+            o = sparse_decode(q, k_cache, v_cache, block_table, seq_lens, tk_all[g], T, sm_scale,
+                              k_scale, v_scale, n_range=n_range, threads=threads)
+            if out is None:
+                out = o.copy()
+            out[:, g * G:(g + 1) * G] = o[:, g * G:(g + 1) * G]
+        return out
     lib = _load()
     qa, qd = _raw(q)
     ka, kvd = _raw(k_cache)
     va, _ = _raw(v_cache)
     bt, _ = _raw(block_table)
     sl, _ = _raw(seq_lens)
-    tk, _ = _raw(torch.as_tensor(topk_idx, dtype=torch.int32))
+    tk, _ = _raw(torch.as_tensor(tk_all, dtype=torch.int32))
     R, MB = bt.shape
     P, B, Hkv, D = ka.shape
     N, Hq, _ = qa.shape

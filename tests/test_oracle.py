@@ -107,10 +107,12 @@ def brute_scores(case):
 
 
 def brute_attention(case, topk):
-    """Masked dense softmax over [N, Hq, L] built from numpy matmuls."""
+    """Masked dense softmax over [N, Hq, L] built from numpy matmuls.  topk is
+    [N, K] (shared by the KV heads) or [Hkv, N, K] (one selection per KV head)."""
     q = _decode(case.q)
     N, Hq, D = q.shape
     G = case.Hq // case.Hkv
+    per_head = np.ndim(topk) == 3
     out = np.zeros((N, Hq, D))
     for r in range(case.R):
         L = int(case.seq_lens[r])
@@ -120,15 +122,15 @@ def brute_attention(case, topk):
         Vf = _dense_keys(case, case.v_cache, r) * case.v_scale
         for t in range(case.T):
             n = r * case.T + t
-            sel = np.zeros(L, dtype=bool)
-            for j in topk[n]:
-                if 0 <= j < case.MB:
-                    sel[j * case.B:(j + 1) * case.B] = True
-            sel &= np.arange(L) < case.visible(n)
-            if not sel.any():
-                continue
             for h in range(Hq):
                 g = h // G
+                sel = np.zeros(L, dtype=bool)
+                for j in (topk[g][n] if per_head else topk[n]):
+                    if 0 <= j < case.MB:
+                        sel[j * case.B:(j + 1) * case.B] = True
+                sel &= np.arange(L) < case.visible(n)
+                if not sel.any():
+                    continue
                 logits = case.sm_scale * (Kf[sel, g] @ q[n, h])
                 w = np.exp(logits - logits.max())
                 out[n, h] = (w / w.sum()) @ Vf[sel, g]
@@ -165,6 +167,42 @@ def test_attention_matches_brute_force(orc, case):
                             topk, case.T, case.sm_scale, case.k_scale, case.v_scale)
     ref = brute_attention(case, topk)
     np.testing.assert_allclose(got, ref, rtol=1e-11, atol=1e-12)
+
+
+def test_attention_per_kv_head_selection(orc):
+    """attention.decode's (Hkv, B, K) selection: KV head g's query heads attend
+    topk[g] only.  Different random selections per head against brute force,
+    and a head that selects every block against dense attention."""
+    case = synth.make_case("b4_fp32_hkv2", R=2, T=3, Hq=4, Hkv=2, D=8, Di=4, seq_lens=[13, 7],
+                           P=12, k=2, fp8=False, seed=1, B=4)
+    tk = np.stack([synth.random_topk(case, seed=5).numpy(), synth.random_topk(case, seed=6).numpy()])
+    assert not np.array_equal(tk[0], tk[1])
+    got = orc.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                            tk, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    np.testing.assert_allclose(got, brute_attention(case, tk), rtol=1e-11, atol=1e-12)
+    every = np.tile(np.arange(case.MB, dtype=np.int32), (case.N, 1))
+    first = np.full_like(every, -1)
+    first[:, :tk.shape[2]] = tk[0]
+    mixed = np.stack([first, every])
+    got = orc.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                            mixed, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    dense = orc.dense_attention(case.q, case.k_cache, case.v_cache, case.block_table,
+                                case.seq_lens, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    np.testing.assert_allclose(got[:, 2:], dense[:, 2:], rtol=1e-11, atol=1e-12)   # KV head 1
+    np.testing.assert_allclose(got[:, :2], brute_attention(case, tk[0])[:, :2], rtol=1e-11, atol=1e-12)
+
+
+def test_attention_bf16_cache_matches_brute_force(orc):
+    """A dense bf16 K/V cache (attention.decode's commissioned cache): the
+    oracle reads the bf16 values exactly."""
+    case = synth.make_case("b4_bf16kv", R=2, T=3, Hq=4, Hkv=2, D=8, Di=4, seq_lens=[13, 7], P=12,
+                           k=2, fp8=False, seed=7, B=4)
+    case.k_cache = case.k_cache.to(torch.bfloat16)
+    case.v_cache = case.v_cache.to(torch.bfloat16)
+    topk = synth.random_topk(case, seed=8).numpy()
+    got = orc.sparse_decode(case.q, case.k_cache, case.v_cache, case.block_table, case.seq_lens,
+                            topk, case.T, case.sm_scale, case.k_scale, case.v_scale)
+    np.testing.assert_allclose(got, brute_attention(case, topk), rtol=1e-11, atol=1e-12)
 
 
 @pytest.mark.parametrize("case", small_cases(), ids=lambda c: c.name)

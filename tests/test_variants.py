@@ -1,0 +1,114 @@
+"""GPU parity of the attention-boundary variants of attention.decode (Cacheon
+"Kernel ABI", "Attention block slots"): a selection per KV head in the
+(Hkv, B, K) layout, and the dense bf16 K/V cache.  Each is compared with the
+oracle on the same inputs to the attention bar (bf16-rounded outputs within
+2e-3 max-abs)."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from msa_harness import check_attention, oracle_attention, poisoned, upload, workspace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def msa():
+    import block_sparse_paged_amd as m
+    return m
+
+
+def per_head_topk(case, seeds):
+    """[Hkv, N, k] int32: an independent random selection per KV head."""
+    tk = np.stack([synth.random_topk(case, seed=s).numpy() for s in seeds])
+    for g in range(1, tk.shape[0]):
+        assert not np.array_equal(tk[0], tk[g])
+    return tk
+
+
+def attend(msa, case, d, topk, out_dtype=torch.bfloat16):
+    out = poisoned((case.N, case.Hq, case.D), out_dtype)
+    msa.msa_sparse_decode(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, topk, case.T, out,
+                          case.sm_scale, case.k_scale, case.v_scale, case.B,
+                          workspace(msa, case, topk.shape[-1]))
+    torch.cuda.synchronize()
+    return out
+
+
+PER_HEAD = [
+    # MFMA path: bf16 queries, FP8 caches, 16 query heads per KV head
+    dict(R=2, T=4, Hq=32, Hkv=2, D=128, Di=128, seq_lens=[900, 2100], P=30, k=5),
+    # vector path: 4 query heads per KV head, D = 64
+    dict(R=2, T=3, Hq=8, Hkv=2, D=64, Di=64, seq_lens=[700, 1300], P=20, k=4),
+]
+
+
+@pytest.mark.parametrize("spec", PER_HEAD, ids=["mfma_hkv2", "valu_g4"])
+def test_selection_per_kv_head(msa, spec):
+    c = synth.make_case("per_head", seed=61, **spec)
+    print(f"case per_head {spec}", flush=True)
+    d = upload(c)
+    tk = per_head_topk(c, seeds=range(62, 62 + c.Hkv))
+    out = attend(msa, c, d, torch.from_numpy(tk).cuda())
+    check_attention(out, oracle_attention(c, tk))
+
+
+def test_selection_per_kv_head_identical_heads_equal_shared(msa):
+    """[Hkv, N, k] holding the same selection for every KV head gives the
+    shared-selection result bit for bit (also through non-contiguous views)."""
+    c = synth.make_case("per_head_same", R=2, T=4, Hq=32, Hkv=2, D=128, Di=128,
+                        seq_lens=[1000, 1800], P=30, k=6, seed=63)
+    d = upload(c)
+    tk = synth.random_topk(c, seed=64).cuda()
+    shared = attend(msa, c, d, tk)
+    stacked = tk.unsqueeze(0).expand(c.Hkv, -1, -1)          # KV-head stride 0
+    per_head = attend(msa, c, d, stacked)
+    copied = attend(msa, c, d, stacked.contiguous())
+    assert torch.equal(shared.view(torch.int16), per_head.view(torch.int16))
+    assert torch.equal(shared.view(torch.int16), copied.view(torch.int16))
+
+
+BF16_KV = [
+    dict(R=2, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[900, 1700], P=25, k=5, qbf16=True),
+    dict(R=2, T=3, Hq=8, Hkv=2, D=64, Di=64, seq_lens=[600, 1300], P=20, k=4, qbf16=False),
+]
+
+
+@pytest.mark.parametrize("spec", BF16_KV, ids=["bf16q_d128", "f32q_d64_hkv2"])
+def test_bf16_kv_cache(msa, spec):
+    spec = dict(spec)
+    qbf16 = spec.pop("qbf16")
+    c = synth.make_case("bf16kv", fp8=False, seed=65, **spec)
+    c.k_cache = c.k_cache.to(torch.bfloat16)
+    c.v_cache = c.v_cache.to(torch.bfloat16)
+    if qbf16:
+        c.q = c.q.to(torch.bfloat16)
+    print(f"case bf16kv {spec} qbf16={qbf16}", flush=True)
+    d = upload(c)
+    tk = synth.random_topk(c, seed=66)
+    out = attend(msa, c, d, tk.cuda(), out_dtype=torch.bfloat16)
+    check_attention(out, oracle_attention(c, tk.numpy()))
+    # per-KV-head selection on the bf16 cache as well
+    if c.Hkv > 1:
+        tk3 = per_head_topk(c, seeds=range(67, 67 + c.Hkv))
+        out = attend(msa, c, d, torch.from_numpy(tk3).cuda(), out_dtype=torch.bfloat16)
+        check_attention(out, oracle_attention(c, tk3))
+
+
+def test_per_head_selection_shape_is_checked(msa):
+    c = synth.make_case("per_head_bad", R=1, T=2, Hq=32, Hkv=2, D=128, Di=128, seq_lens=[600],
+                        P=10, k=3, seed=68)
+    d = upload(c)
+    bad = torch.zeros((3, c.N, c.k), dtype=torch.int32, device="cuda")     # 3 != Hkv
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    with pytest.raises(msa.MsaError, match="sizes disagree"):
+        msa.msa_sparse_decode(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, bad, c.T, out,
+                              c.sm_scale, c.k_scale, c.v_scale, c.B, workspace(msa, c, c.k))
+    # the selecting calls write one selection for every KV head: [N, k] only
+    scores = torch.zeros((c.N, c.MB), dtype=torch.float32, device="cuda")
+    tk3 = torch.zeros((c.Hkv, c.N, c.k), dtype=torch.int32, device="cuda")
+    with pytest.raises(msa.MsaError):
+        msa.msa_select_sparse_decode(scores, c.k, tk3, d.q, d.k_cache, d.v_cache, d.block_table,
+                                     d.seq_lens, c.T, out, c.sm_scale, c.k_scale, c.v_scale, c.B,
+                                     workspace(msa, c, c.k))
