@@ -278,7 +278,7 @@ int32_t run_select_attn(const TopkParams &tk, AttnParams &at, const AttnPlan &pl
     if (plan.mfma && tk.MB <= kSelectInAttnMaxMB) {
         at.scores = tk.scores; at.sc_sn = tk.sc_sn; at.sc_sj = tk.sc_sj;
         at.topk_out = tk.topk;
-        return launch_attention_select(at, D, stream) == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
+        return launch_attention_select(at, D, kvt, stream) == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
     }
     if (launch_topk(tk, stream) != hipSuccess) return MSA_ERR_LAUNCH;
     return run_attn(at, plan, qt, kvt, D, stream);

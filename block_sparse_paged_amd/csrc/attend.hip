@@ -156,19 +156,19 @@ __device__ __forceinline__ TokenSlot decode_token_slot(const AttnParams &p) {
     return q;
 }
 
-template <int D>
+template <int D, int KV>
 __global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_token_kernel(AttnParams p) {
     const TokenSlot q = decode_token_slot(p);
     if (!q.live) return;                         // uniform over the workgroup
-    attn_unit<D, false>(p, q.n, q.g, q.s);
+    attn_unit<D, false, KV>(p, q.n, q.g, q.s);
 }
 
 // The same, selecting the token's blocks from its score row first (MB <= 128).
-template <int D>
+template <int D, int KV>
 __global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_token_select_kernel(AttnParams p) {
     const TokenSlot q = decode_token_slot(p);
     if (!q.live) return;
-    attn_unit<D, true>(p, q.n, q.g, q.s);
+    attn_unit<D, true, KV>(p, q.n, q.g, q.s);
 }
 
 // ------------------------------------------------------------------ VALU path
@@ -370,15 +370,15 @@ static int64_t token_grid(const AttnParams &p) {
     return 8 * units_per_xcd * p.splits;
 }
 
-template <int D>
+template <int D, int KV>
 hipError_t launch_token(const AttnParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((attn_token_kernel<D>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_token_kernel<D, KV>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
     return hipGetLastError();
 }
 
-template <int D>
+template <int D, int KV>
 hipError_t launch_token_select(const AttnParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((attn_token_select_kernel<D>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_token_select_kernel<D, KV>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
     return hipGetLastError();
 }
 
@@ -418,7 +418,7 @@ static void token_split(int32_t k, int32_t *S, int32_t *bpw) {
 }
 
 bool attention_uses_mfma(int q_type, int kv_type, int G) {
-    return G == 16 && q_type == E_BF16 && kv_type == E_FP8;
+    return G == 16 && q_type == E_BF16 && (kv_type == E_FP8 || kv_type == E_BF16);
 }
 
 AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type) {
@@ -470,16 +470,20 @@ hipError_t launch_attention(const AttnParams &p, int q_type, int kv_type, int D,
     const int64_t grid = (int64_t)p.R * p.Hkv * TG * p.splits;
     if (grid == 0) return hipSuccess;
     const int G = p.Hq / p.Hkv;
-    if (attention_uses_mfma(q_type, kv_type, G))
-        return D == 64 ? launch_token<64>(p, s) : launch_token<128>(p, s);
+    if (attention_uses_mfma(q_type, kv_type, G)) {
+        if (kv_type == E_BF16) return D == 64 ? launch_token<64, E_BF16>(p, s) : launch_token<128, E_BF16>(p, s);
+        return D == 64 ? launch_token<64, E_FP8>(p, s) : launch_token<128, E_FP8>(p, s);
+    }
     return D == 64 ? launch_valu_types<64>(p, q_type, kv_type, grid, s)
                    : launch_valu_types<128>(p, q_type, kv_type, grid, s);
 }
 
-hipError_t launch_attention_select(const AttnParams &p, int D, hipStream_t s) {
+hipError_t launch_attention_select(const AttnParams &p, int D, int kv_type, hipStream_t s) {
     if ((int64_t)p.R * p.T * p.Hkv == 0) return hipSuccess;
     if (p.MB > kSelSlots || p.k > p.MB) return hipErrorInvalidValue;
-    return D == 64 ? launch_token_select<64>(p, s) : launch_token_select<128>(p, s);
+    if (kv_type == E_BF16)
+        return D == 64 ? launch_token_select<64, E_BF16>(p, s) : launch_token_select<128, E_BF16>(p, s);
+    return D == 64 ? launch_token_select<64, E_FP8>(p, s) : launch_token_select<128, E_FP8>(p, s);
 }
 
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s) {

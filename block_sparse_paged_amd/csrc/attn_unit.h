@@ -54,6 +54,7 @@ constexpr bool kKFirst = MSA_ATTN_KFIRST;       // issue all K rows before the V
 // once.  Correctness does not depend on the placement.
 
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
 
 // 16 bytes per lane from global memory straight into LDS (the 64 lanes' data
 // land contiguously from lds, which must be wave-uniform), non-temporal.
@@ -126,23 +127,43 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// BF16 caches (attention.decode's dense cache): rows of 2*D bytes, so a wave
+// takes 32 keys of a page (four waves per page, two page slots, twice the
+// pages per wave: the same selection entries per workgroup) in 16-key LDS
+// sub-chunks of the same size as the FP8 ones.  K fragments are read as they
+// are; V^T fragments come from two ds_read_b64_tr_b16, each handing a lane 4
+// keys at one d (lane i of a 16-lane group gets element i%4 of the 8-byte
+// reads of lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4).  16-byte units of both are
+// XOR-swizzled by key & (units per row - 1).
+__device__ __forceinline__ uint4 bf16x4x2(v2i a, v2i b) {
+    return make_uint4((uint32_t)a.x, (uint32_t)a.y, (uint32_t)b.x, (uint32_t)b.y);
+}
+
 // SEL: the token's selection is computed here from its score row (MB <= 128;
 // by wave 0, into LDS slots) instead of read from topk_idx, and the workgroup
-// of split 0, KV head 0 writes it to topk_idx.
-template <int D, bool SEL>
+// of split 0, KV head 0 writes it to topk_idx.  KV: E_FP8 or E_BF16 caches.
+template <int D, bool SEL, int KV = E_FP8>
 __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, const int g, const int qs) {
+    constexpr bool BF = KV == E_BF16;
     constexpr int NW = kAttnWaves;
     constexpr int KS = D / 32;          // k-steps of the QK product
     constexpr int DT = D / 16;          // 16-row d tiles of the PV product
-    constexpr int CPR = D / 16;         // 16-byte units per key row
+    constexpr int RB = BF ? 2 * D : D;  // bytes per K (V) row
+    constexpr int CPR = RB / 16;        // 16-byte units per key row
     constexpr int KPL = 64 / CPR;       // keys per 1 KiB direct-to-LDS load
-    constexpr int LPC = kChunk / KPL;   // loads per sub-chunk, for K and for V
-    constexpr int CB = kChunk * D;      // bytes of one sub-chunk's K (or V) rows
-    static_assert(CB % 1024 == 0 && LPC >= 1 && KPL % 8 == 0, "sub-chunk layout");
-    constexpr int CK = kPipeKeys;       // keys per pipeline chunk (softmax update)
-    constexpr int NS = CK / kChunk;     // sub-chunks per pipeline chunk
-    constexpr int NC = kWaveKeys / CK;  // pipeline chunks per wave and page
-    static_assert(NS >= 1 && NC >= 1 && NS * NC == kWaveChunks, "pipeline chunk");
+    constexpr int CHK = BF ? 16 : kChunk;   // keys per sub-chunk
+    constexpr int WK = BF ? 32 : kWaveKeys; // keys of a page per wave
+    constexpr int WPP = kBlock / WK;    // waves per page
+    constexpr int SLOTS = NW / WPP;     // page slots per workgroup
+    constexpr int LPC = CHK / KPL;      // loads per sub-chunk, for K and for V
+    constexpr int CB = CHK * RB;        // bytes of one sub-chunk's K (or V) rows
+    static_assert(CB % 1024 == 0 && LPC >= 1 && (BF || KPL % 8 == 0), "sub-chunk layout");
+    static_assert(WK / CHK == kWaveChunks, "two sub-chunks per wave");
+    constexpr int CK = BF ? 32 : kPipeKeys;  // keys per pipeline chunk (softmax update)
+    constexpr int NS = CK / CHK;        // sub-chunks per pipeline chunk
+    constexpr int NC = WK / CK;         // pipeline chunks per wave and page
+    constexpr int TPS = CHK / 16;       // 16-key QK tiles per sub-chunk
+    static_assert(NS >= 1 && NC >= 1 && NS * NC == kWaveChunks && CK == 32, "pipeline chunk");
     // per sub-chunk, [8 waves][32 keys][D bytes]; the wave merge reuses lk0, lk1
     __shared__ __attribute__((aligned(16))) uint8_t lk0[NW * CB], lk1[NW * CB];
     __shared__ __attribute__((aligned(16))) uint8_t lv0[NW * CB], lv1[NW * CB];
@@ -153,9 +174,10 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pslot = wave >> 1, half = wave & 1;
+    const int pslot = wave / WPP, half = wave % WPP;
+    const int bpw = p.bpw * 4 / SLOTS;          // pages per wave (the same entries per workgroup)
     const int r = n / p.T, t = n % p.T;
-    const int per_wg = 4 * p.bpw;
+    const int per_wg = SLOTS * bpw;
     const int e0 = qs * per_wg;
     const int e1 = min(p.k, e0 + per_wg);
     const int h0 = g * 16;
@@ -220,8 +242,8 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     uint8_t *const kc[kWaveChunks] = {lk0 + wave * CB, lk1 + wave * CB};
     uint8_t *const vc[kWaveChunks] = {lv0 + wave * CB, lv1 + wave * CB};
     const int grp = lane >> 4, li = lane & 15;
-    for (int b = 0; b < p.bpw; ++b) {
-        const int i = e0 + pslot * p.bpw + b;
+    for (int b = 0; b < bpw; ++b) {
+        const int i = e0 + pslot * bpw + b;
         if (i >= e1) break;
         // entry i and duplicate check against entries [0, i)  (wave-uniform)
         int j;
@@ -241,8 +263,8 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
             }
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
-        // this wave's keys of the page: kbase .. kbase + 63 (the first visible)
-        const int kbase = j * kBlock + half * kWaveKeys;
+        // this wave's keys of the page: kbase .. kbase + WK - 1 (the first visible)
+        const int kbase = j * kBlock + half * WK;
         if (dup || j < 0 || j >= p.MB || kbase >= vis) continue;
         int pid;
         if (j < 128) {
@@ -252,10 +274,12 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         }
         if (pid < 0 || pid >= p.P) continue;
-        const uint8_t *kp = (const uint8_t *)p.k_cache + (int64_t)pid * p.k_sp + (int64_t)g * p.k_sh +
-                            (int64_t)(half * kWaveKeys) * p.k_sb;
-        const uint8_t *vp = (const uint8_t *)p.v_cache + (int64_t)pid * p.v_sp + (int64_t)g * p.v_sh +
-                            (int64_t)(half * kWaveKeys) * p.v_sb;
+        // element strides: bytes for FP8, 2 bytes per element for bf16
+        const uint8_t *kp = (const uint8_t *)p.k_cache + ((int64_t)pid * p.k_sp + (int64_t)g * p.k_sh +
+                                                          (int64_t)(half * WK) * p.k_sb) * (BF ? 2 : 1);
+        const uint8_t *vp = (const uint8_t *)p.v_cache + ((int64_t)pid * p.v_sp + (int64_t)g * p.v_sh +
+                                                          (int64_t)(half * WK) * p.v_sb) * (BF ? 2 : 1);
+        const int64_t ksb = p.k_sb * (BF ? 2 : 1), vsb = p.v_sb * (BF ? 2 : 1);   // row strides in bytes
         // the previous page's LDS reads have all returned before its slots are refilled
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         // Issue the K and V rows of the page.  Load l of a 32-key sub-chunk
@@ -267,18 +291,25 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         // sub-chunks (kKFirst: all K, then all V).
         {
             const int key0 = lane / CPR, slot = lane % CPR;
-            const uint8_t *ka = kp + (int64_t)key0 * p.k_sb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
+            const uint8_t *ka = kp + (int64_t)key0 * ksb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
             auto issue_k = [&](int sc) {
 #pragma unroll
-                for (int l = 0; l < LPC; ++l)
-                    dma16_nt(ka + (int64_t)(sc * kChunk + l * KPL) * p.k_sb, kc[sc] + l * 1024);
+                for (int l = 0; l < LPC; ++l) {
+                    if constexpr (BF) {
+                        const int key = l * KPL + key0;
+                        dma16_nt(kp + (int64_t)(sc * CHK + key) * ksb + ((slot ^ (key & (CPR - 1))) << 4),
+                                 kc[sc] + l * 1024);
+                    } else {
+                        dma16_nt(ka + (int64_t)(sc * kChunk + l * KPL) * ksb, kc[sc] + l * 1024);
+                    }
+                }
             };
             auto issue_v = [&](int sc) {
 #pragma unroll
                 for (int l = 0; l < LPC; ++l) {
                     const int key = l * KPL + key0;
-                    dma16_nt(vp + (int64_t)(sc * kChunk + key) * p.v_sb + ((slot ^ (vswz(key) & (CPR - 1))) << 4),
-                             vc[sc] + l * 1024);
+                    const int sw = BF ? (key & (CPR - 1)) : (vswz(key) & (CPR - 1));
+                    dma16_nt(vp + (int64_t)(sc * CHK + key) * vsb + ((slot ^ sw) << 4), vc[sc] + l * 1024);
                 }
             };
             if constexpr (kKFirst) {
@@ -296,12 +327,12 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                 }
             }
         }
-        const bool full = kbase + kWaveKeys <= vis;    // every key visible to this token
+        const bool full = kbase + WK <= vis;           // every key visible to this token
         // V rows past seq_len hold arbitrary bytes (NaN poison in the tests);
         // their P is 0, but 0 * NaN would poison the sum, so such keys are
         // dropped from the operand (only on the page holding seq_len)
         const int vvalid = L - kbase;
-        const bool vfull = vvalid >= kWaveKeys;
+        const bool vfull = vvalid >= WK;
         static_for<0, NC>([&](auto C) {
             constexpr int c = decltype(C)::value;
             // loads issued after the last K (V) load of chunk c
@@ -313,36 +344,47 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
             // S^T tiles: sacc[u][e] = q . k for key c*CK + 16*u + 4*grp + e and
             // head h0 + lane%16.  A operand: key 16*(u%2) + lane%16 of sub-chunk
             // c*NS + u/2, d = (D/4)*grp + 8*ks .. +8
-            f32x4 sacc[2 * NS];
+            f32x4 sacc[2];
 #pragma unroll
-            for (int u = 0; u < 2 * NS; ++u) {
-                const int key = (u & 1) * 16 + li;
-                const uint8_t *krow = kc[c * NS + u / 2] + key * D;
-                const int ksw = key & (CPR - 1) & 7;
+            for (int u = 0; u < 2; ++u) {
+                const int key = (u % TPS) * 16 + li;
+                const uint8_t *krow = kc[c * NS + u / TPS] + key * RB;
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (BF) {
+                    // k-step ks, lane group grp: d = (D/4)*grp + 8*ks .. +8, one 16-byte unit
 #pragma unroll
-                for (int kp2 = 0; kp2 < KS / 2; ++kp2) {
-                    const int unit = ((D / 4) * grp) / 16 + kp2;
-                    const uint4 raw = *(const uint4 *)(krow + ((unit ^ ksw) << 4));
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(raw.x, raw.y)),
-                        __builtin_bit_cast(bf16x8, qf[2 * kp2]), acc, 0, 0, 0);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(raw.z, raw.w)),
-                        __builtin_bit_cast(bf16x8, qf[2 * kp2 + 1]), acc, 0, 0, 0);
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const int unit = (D / 32) * grp + ks;
+                        const uint4 a = *(const uint4 *)(krow + ((unit ^ (key & (CPR - 1))) << 4));
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), acc, 0, 0, 0);
+                    }
+                } else {
+                    const int ksw = key & (CPR - 1) & 7;
+#pragma unroll
+                    for (int kp2 = 0; kp2 < KS / 2; ++kp2) {
+                        const int unit = ((D / 4) * grp) / 16 + kp2;
+                        const uint4 raw = *(const uint4 *)(krow + ((unit ^ ksw) << 4));
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(raw.x, raw.y)),
+                            __builtin_bit_cast(bf16x8, qf[2 * kp2]), acc, 0, 0, 0);
+                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(raw.z, raw.w)),
+                            __builtin_bit_cast(bf16x8, qf[2 * kp2 + 1]), acc, 0, 0, 0);
+                    }
                 }
                 sacc[u] = acc * scale2;
             }
             if (!full) {
 #pragma unroll
-                for (int u = 0; u < 2 * NS; ++u)
+                for (int u = 0; u < 2; ++u)
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         sacc[u][e] = (kbase + c * CK + u * 16 + 4 * grp + e < vis) ? sacc[u][e] : -INFINITY;
             }
             float cmax = -INFINITY;
 #pragma unroll
-            for (int u = 0; u < 2 * NS; ++u)
+            for (int u = 0; u < 2; ++u)
                 cmax = fmaxf(cmax, fmaxf(fmaxf(sacc[u][0], sacc[u][1]), fmaxf(sacc[u][2], sacc[u][3])));
             cmax = max_across_groups<16>(cmax);
             // chunk 0 holds the wave's first key of the page, which is visible:
@@ -352,10 +394,10 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
             m_run = m_new;
             // P rounded to bf16 (hardware RNE); l sums the rounded values so
             // that the weights used in PV and in the normaliser are the same
-            uint32_t pb[2 * NS][2];
+            uint32_t pb[2][2];
             float lsum = 0.f;
 #pragma unroll
-            for (int u = 0; u < 2 * NS; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int hh = 0; hh < 2; ++hh) {
                     const uint32_t w = cvt_pk_bf16(exp2_fast(sacc[u][2 * hh] - m_new),
@@ -368,14 +410,43 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
             // ---- V rows of chunk c landed
             wait_vmcnt<after_v>();
-            // lanes 2b, 2b+1 of a 16-lane group read the two 8-byte halves of
-            // key pv_key(grp, b)'s 16-byte unit dt
-            const int key = pv_key(grp, li >> 1);
-            const int vsw = vswz(key) & (CPR - 1);
+            const uint4 bp = make_uint4(pb[0][0], pb[0][1], pb[1][0], pb[1][1]);
+            if constexpr (BF) {
+                // V^T A operand of the 32-key chunk: k index 8*grp + e holds key
+                // pv_key(grp, e) = sub-chunk e/4, key 4*grp + e%4; lane li of the
+                // group reads 4 d of key 4*grp + li/4 (d 16*dt + 4*(li%4) ..)
+                const int vk = 4 * grp + (li >> 2);
+                const int vq = li & 3;
+                uint32_t kill[2][2] = {{0u, 0u}, {0u, 0u}};
+                if (!vfull) {
 #pragma unroll
-            for (int u = 0; u < NS; ++u) {
-                const int sc = c * NS + u;
-                const uint4 bp = make_uint4(pb[2 * u][0], pb[2 * u][1], pb[2 * u + 1][0], pb[2 * u + 1][1]);
+                    for (int e = 0; e < 8; ++e) {
+                        const bool dead = c * CK + pv_key(grp, e) >= vvalid;
+                        const uint32_t m = dead ? (0xffffu << (16 * (e & 1))) : 0u;
+                        kill[e >> 2][(e >> 1) & 1] |= m;
+                    }
+                }
+                const uint8_t *v0 = vc[c * NS] + vk * RB + 8 * (vq & 1);
+                const uint8_t *v1 = vc[c * NS + 1] + vk * RB + 8 * (vq & 1);
+                const int vsw = vk & (CPR - 1);
+#pragma unroll
+                for (int dt = 0; dt < DT; ++dt) {
+                    const int unit = 2 * dt + (vq >> 1);
+                    v2i r0 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)(v0 + ((unit ^ vsw) << 4))));
+                    v2i r1 = __builtin_bit_cast(v2i, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) v4i16 *)(v1 + ((unit ^ vsw) << 4))));
+                    r0.x &= ~kill[0][0]; r0.y &= ~kill[0][1];
+                    r1.x &= ~kill[1][0]; r1.y &= ~kill[1][1];
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf16x4x2(r0, r1)),
+                                                                    __builtin_bit_cast(bf16x8, bp), o[dt], 0, 0, 0);
+                }
+            } else {
+                // lanes 2b, 2b+1 of a 16-lane group read the two 8-byte halves of
+                // key pv_key(grp, b)'s 16-byte unit dt
+                const int key = pv_key(grp, li >> 1);
+                const int vsw = vswz(key) & (CPR - 1);
+                const int sc = c * NS;
                 const uint8_t *vrow = vc[sc] + key * D + 8 * (li & 1);
                 uint32_t kill_lo = 0u, kill_hi = 0u;
                 if (!vfull) {

@@ -77,7 +77,7 @@ __host__ __device__ __forceinline__ int64_t part_acc_index(int s, int64_t n, int
 // Attention that computes each token's selection from the score sheet first
 // (the decode step's second launch); MB <= 128.  Like the MFMA path of
 // launch_attention it merges its splits itself.
-hipError_t launch_attention_select(const AttnParams &p, int D, hipStream_t s);
+hipError_t launch_attention_select(const AttnParams &p, int D, int kv_type, hipStream_t s);
 constexpr int kSelectInAttnMaxMB = 128;
 
 // Split plan of msa_sparse_decode for the given sizes and element types.

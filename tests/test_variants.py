@@ -70,21 +70,31 @@ def test_selection_per_kv_head_identical_heads_equal_shared(msa):
 
 
 BF16_KV = [
+    # MFMA path (bf16 queries, 16 query heads per KV head)
     dict(R=2, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[900, 1700], P=25, k=5, qbf16=True),
+    dict(R=3, T=4, Hq=16, Hkv=1, D=64, Di=64, seq_lens=[129, 2000, 3333], P=50, k=9, qbf16=True),
+    dict(R=2, T=4, Hq=32, Hkv=2, D=128, Di=128, seq_lens=[1000, 4000], P=45, k=16, qbf16=True),
+    dict(R=1, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[16000], P=130, k=40, qbf16=True),
+    # vector path (f32 queries, 4 query heads per KV head)
     dict(R=2, T=3, Hq=8, Hkv=2, D=64, Di=64, seq_lens=[600, 1300], P=20, k=4, qbf16=False),
 ]
 
 
-@pytest.mark.parametrize("spec", BF16_KV, ids=["bf16q_d128", "f32q_d64_hkv2"])
-def test_bf16_kv_cache(msa, spec):
+def bf16_case(spec, seed):
     spec = dict(spec)
     qbf16 = spec.pop("qbf16")
-    c = synth.make_case("bf16kv", fp8=False, seed=65, **spec)
+    c = synth.make_case("bf16kv", fp8=False, seed=seed, **spec)
     c.k_cache = c.k_cache.to(torch.bfloat16)
     c.v_cache = c.v_cache.to(torch.bfloat16)
     if qbf16:
         c.q = c.q.to(torch.bfloat16)
-    print(f"case bf16kv {spec} qbf16={qbf16}", flush=True)
+    return c
+
+
+@pytest.mark.parametrize("spec", BF16_KV, ids=["d128", "d64_ragged", "hkv2_k16", "k40_16k", "valu_f32q"])
+def test_bf16_kv_cache(msa, spec):
+    c = bf16_case(spec, seed=65)
+    print(f"case bf16kv {spec}", flush=True)
     d = upload(c)
     tk = synth.random_topk(c, seed=66)
     out = attend(msa, c, d, tk.cuda(), out_dtype=torch.bfloat16)
@@ -94,6 +104,29 @@ def test_bf16_kv_cache(msa, spec):
         tk3 = per_head_topk(c, seeds=range(67, 67 + c.Hkv))
         out = attend(msa, c, d, torch.from_numpy(tk3).cuda(), out_dtype=torch.bfloat16)
         check_attention(out, oracle_attention(c, tk3))
+
+
+def test_bf16_kv_cache_select_path(msa):
+    """msa_select_sparse_decode on a bf16 cache (selection inside the attention
+    launch): its selection is the oracle's on the same sheet and its output
+    equals msa_sparse_decode's over that selection, bit for bit."""
+    import oracle
+    c = bf16_case(dict(R=2, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[3000, 1500], P=40, k=8,
+                       qbf16=True), seed=69)
+    d = upload(c)
+    sheet = np.random.default_rng(70).standard_normal((c.N, c.MB)).astype(np.float32)
+    scores = torch.from_numpy(sheet).cuda()
+    tk = poisoned((c.N, c.k), torch.int32)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    ws = workspace(msa, c, c.k)
+    msa.msa_select_sparse_decode(scores, c.k, tk, d.q, d.k_cache, d.v_cache, d.block_table,
+                                 d.seq_lens, c.T, out, c.sm_scale, c.k_scale, c.v_scale, c.B, ws)
+    torch.cuda.synchronize()
+    gt = tk.cpu().numpy()
+    assert np.array_equal(gt, oracle.select_topk(sheet.astype(np.float64), c.k))
+    out2 = attend(msa, c, d, tk)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    check_attention(out, oracle_attention(c, gt))
 
 
 def test_per_head_selection_shape_is_checked(msa):
