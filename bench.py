@@ -58,6 +58,8 @@ def parse():
                          "8 times, as the reference for HBM byte counters")
     ap.add_argument("--calib-out", default=os.path.join(ROOT, "gpurun_out"),
                     help="directory for calib.json (the copy size and the calls' algorithmic bytes)")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the dense bf16 K/V attention variant")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script made with --calib-copy-mib, write profiles/traffic.json, print a "
@@ -202,6 +204,53 @@ def prefill_score(torch, msa, synth, copies: int = 4, reps: int = 50) -> dict:
             "roofline": {"bound": "mfma", "kernel": "score_prefill_kernel<128, 4>", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
+def bf16_kv_attention(torch, msa, case, topk, copies: int = 4, reps: int = 50) -> dict:
+    """msa_sparse_decode over the same selection with the caches held as dense
+    bf16 (attention.decode's commissioned cache; the FP8 values widened
+    exactly), timed alone on cold pool copies like the decode calls."""
+    dev = "cuda"
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    k0 = f8(case.k_cache).to(dev).to(torch.bfloat16)
+    v0 = f8(case.v_cache).to(dev).to(torch.bfloat16)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    q, bt, sl = case.q.to(dev), case.block_table.to(dev), case.seq_lens.to(dev)
+    tk = torch.from_numpy(topk).to(dev)
+    out = torch.empty((case.N, case.Hq, case.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D,
+                                                           case.k), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def body():
+        for kc, vc in pools:
+            msa.msa_sparse_decode(q, kc, vc, bt, sl, tk, case.T, out, case.sm_scale, case.k_scale,
+                                  case.v_scale, case.B, ws)
+    with torch.cuda.stream(stream):
+        body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1000.0 / (reps * copies)
+    ab = algorithmic_bytes(case, topk)
+    nbytes = ab["decode"] + ab["kv"]            # the K/V rows count twice at 2 bytes per element
+    gbs = nbytes / t / 1e9
+    return {"workload": "msa_sparse_decode, 16 rows x 4 tokens, 16384 ctx, top-k 16, dense bf16 K/V caches",
+            "us": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "kernel": "attn_token_kernel<128, bf16>", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
 def cpu_baseline(case, min_wall: float = 1.0) -> dict:
@@ -381,6 +430,9 @@ def main():
     }
     if not a.no_prefill:
         res["prefill_score"] = prefill_score(torch, msa, synth)
+    if not a.no_variants:
+        del pools, scores, out, ws
+        res["bf16_kv_attention"] = bf16_kv_attention(torch, msa, case, tk_host)
     if a.calib_copy_mib > 0:
         # the reference copy's size and the calls' algorithmic bytes, for --pmc-summary
         os.makedirs(a.calib_out, exist_ok=True)
