@@ -218,8 +218,8 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
 // their A operands ready to use: the decode costs 16 VALU instructions per
 // wave and page instead of one per MFMA, and VALU issue does not overlap MFMA
 // issue well on a SIMD.  The next page's slice is loaded into registers while
-// the current page is multiplied, decoded and stored after it (one barrier
-// per page).  Pages that every token sees whole skip the causal mask.  The
+// the current page is multiplied, decoded and stored after it; pages go
+// through LDS two at a time (four bf16 page buffers, one barrier per pair).  Pages that every token sees whole skip the causal mask.  The
 // running block max per (query, block) is staged in LDS and written out
 // coalesced at the end.
 
@@ -234,20 +234,25 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// S^T tile for keys 16*kt .. +15 of the bf16 page in `buf` against the
-// wave's QT query tiles: acc[qt][e] = q . k for key 16*kt + 4*grp + e and
-// query column lane%16.  K-step ks covers d = 32*ks .. +31, lane group grp
-// its d = 32*ks + 8*grp .. +7: 16-byte unit 4*ks + grp of the key's bf16 row,
-// stored XOR-swizzled by the key.
-template <int DI, int QT>
-__device__ __forceinline__ void prefill_tile(const uint8_t *buf, int kt, int li, int grp,
-                                             const uint4 (&qf)[QT][DI / 32], f32x4 (&acc)[QT]) {
+// bf16 A operands of the 16-key tile kt of the page in `buf`: key 16*kt +
+// lane%16; k-step ks covers d = 32*ks .. +31, lane group grp its d = 32*ks +
+// 8*grp .. +7: 16-byte unit 4*ks + grp of the key's bf16 row, stored
+// XOR-swizzled by the key.
+template <int DI>
+__device__ __forceinline__ void prefill_frag(const uint8_t *buf, int kt, int li, int grp, uint4 (&a)[DI / 32]) {
     constexpr int KS = DI / 32, UPR = DI / 8;
     const int key = kt * 16 + li;
     const uint8_t *krow = buf + key * (DI * 2);
-    uint4 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = *(const uint4 *)(krow + (((4 * ks + grp) ^ (key & (UPR - 1))) << 4));
+}
+
+// S^T tile of those keys against the wave's QT query tiles: acc[qt][e] =
+// q . k for key 16*kt + 4*grp + e and query column lane%16.
+template <int DI, int QT>
+__device__ __forceinline__ void prefill_mma(const uint4 (&a)[DI / 32], const uint4 (&qf)[QT][DI / 32],
+                                            f32x4 (&acc)[QT]) {
+    constexpr int KS = DI / 32;
 #pragma unroll
     for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -270,9 +275,9 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
     constexpr int TPK = DI / (16 * VPT);        // slices per key row
     constexpr int NLD = TPK * kBlock;           // threads holding a slice (whole waves)
     static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
-    __shared__ __attribute__((aligned(16))) uint8_t kb[2][kBlock * RB];
+    __shared__ __attribute__((aligned(16))) uint8_t kb[4][kBlock * RB];   // two pairs of pages
     __shared__ float sbuf[PQ][kPMaxPC + 1];
-    static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the page buffers");
+    static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the first pair");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -316,16 +321,16 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
     // this thread's slice of a page (threads below NLD): key tid / TPK, bytes
     // 16*VPT*(tid % TPK) ..
     const int skey = tid / TPK, spart = tid % TPK;
-    uint4 pv[VPT];
-    auto load_page = [&](int pi) {
+    uint4 pv[2][VPT];                                      // the slices of the next pair of pages
+    auto load_page = [&](int pi, uint4 (&v)[VPT]) {
         if (NLD < NT && tid >= NLD) return;
         const int pid = __builtin_amdgcn_readlane(pid_l, pi);
         const uint8_t *src = (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp + (int64_t)skey * p.k_sb +
                              16 * VPT * spart;
 #pragma unroll
-        for (int h = 0; h < VPT; ++h) pv[h] = *(const uint4 *)(src + 16 * h);
+        for (int h = 0; h < VPT; ++h) v[h] = *(const uint4 *)(src + 16 * h);
     };
-    auto store_page = [&](uint8_t *dst) {                  // decode the slice to bf16 into dst
+    auto store_page = [&](const uint4 (&pv)[VPT], uint8_t *dst) {   // decode the slice to bf16 into dst
         if (NLD < NT && tid >= NLD) return;
         uint8_t *row = dst + skey * RB;
 #pragma unroll
@@ -340,10 +345,12 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
             *(uint4 *)(row + (((u0 + 1) ^ (skey & (UPR - 1))) << 4)) = hi;
         }
     };
-    int cur = next_live();
-    // The first page is requested before the query rows: the other order was
-    // measured to be far slower.
-    if (cur >= 0) load_page(cur);
+    // Pages go through LDS two at a time (one barrier per pair).  The first
+    // pair is requested before the query rows: the other order was measured
+    // to be far slower.
+    int c0 = next_live(), c1 = next_live();
+    if (c0 >= 0) load_page(c0, pv[0]);
+    if (c1 >= 0) load_page(c1, pv[1]);
 
     // Query rows, read coalesced.  In the MFMA operand layout consecutive
     // lanes hold different query rows, and a global load in that layout
@@ -402,34 +409,40 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
         }
     }
 
-    // first live page to LDS (once every wave is done with its transpose
-    // area); the second one's slice on its way
+    // first pair to LDS (once every wave is done with its transpose area);
+    // the next pair's slices on their way
     __syncthreads();
-    if (cur >= 0) store_page(kb[0]);
-    int nxt = next_live();
-    if (nxt >= 0) load_page(nxt);
+    if (c0 >= 0) store_page(pv[0], kb[0]);
+    if (c1 >= 0) store_page(pv[1], kb[1]);
+    int n0 = next_live(), n1 = next_live();
+    if (n0 >= 0) load_page(n0, pv[0]);
+    if (n1 >= 0) load_page(n1, pv[1]);
     __syncthreads();
 
     const float scale = p.idx_scale;
-    for (int i = 0; cur >= 0; ++i) {
+    auto compute_page = [&](const uint8_t *buf, int cur) {
         const int kbase = (j0 + cur) * kBlock;
-        const uint8_t *buf = kb[i & 1];
         float best[QT];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) best[qt] = -INFINITY;
         if (kbase + kBlock <= vmin) {                      // every key visible to every token
-            // the max of tile kt is taken after tile kt+1's MFMAs are issued,
-            // so that it runs while they execute instead of waiting for kt's
+            // tile kt+1's operands are read before tile kt's MFMAs, and tile
+            // kt's max is taken after tile kt+1's MFMAs are issued, so that
+            // neither the LDS latency nor the MFMA latency sits in the way
             f32x4 acc[2][QT];
-            prefill_tile<DI, QT>(buf, 0, li, grp, qf, acc[0]);
+            uint4 af[2][KS];
+            prefill_frag<DI>(buf, 0, li, grp, af[0]);
 #pragma unroll
-            for (int kt = 1; kt <= 8; ++kt) {
-                if (kt < 8) prefill_tile<DI, QT>(buf, kt, li, grp, qf, acc[kt & 1]);
-                const f32x4 *done = acc[(kt - 1) & 1];
+            for (int kt = 0; kt <= 8; ++kt) {
+                if (kt + 1 < 8) prefill_frag<DI>(buf, kt + 1, li, grp, af[(kt + 1) & 1]);
+                if (kt < 8) prefill_mma<DI, QT>(af[kt & 1], qf, acc[kt & 1]);
+                if (kt >= 1) {
+                    const f32x4 *done = acc[(kt - 1) & 1];
 #pragma unroll
-                for (int qt = 0; qt < QT; ++qt) {
-                    best[qt] = max3f(best[qt], done[qt][0], done[qt][1]);
-                    best[qt] = max3f(best[qt], done[qt][2], done[qt][3]);
+                    for (int qt = 0; qt < QT; ++qt) {
+                        best[qt] = max3f(best[qt], done[qt][0], done[qt][1]);
+                        best[qt] = max3f(best[qt], done[qt][2], done[qt][3]);
+                    }
                 }
             }
         } else {                                           // causal edge: mask key >= V(token)
@@ -437,8 +450,10 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
 #pragma unroll
             for (int qt = 0; qt < QT; ++qt) lim[qt] = vt[qt] - kbase - 4 * grp;
             for (int kt = 0; kt < 8; ++kt) {
+                uint4 a[KS];
+                prefill_frag<DI>(buf, kt, li, grp, a);
                 f32x4 acc[QT];
-                prefill_tile<DI, QT>(buf, kt, li, grp, qf, acc);
+                prefill_mma<DI, QT>(a, qf, acc);
 #pragma unroll
                 for (int qt = 0; qt < QT; ++qt) {
                     float m[4];
@@ -454,14 +469,22 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
             const float v = max_across_groups<16>(best[qt]);
             if (grp == 0) sbuf[16 * QT * wave + 16 * qt + li][cur] = v * scale;
         }
-        // the other buffer held the previous page, done by every wave before
-        // the last barrier
-        if (nxt >= 0) store_page(kb[(i + 1) & 1]);
-        const int after = next_live();
-        if (after >= 0) load_page(after);
+    };
+    for (int i = 0; c0 >= 0; ++i) {
+        const int b = 2 * (i & 1);
+        compute_page(kb[b], c0);
+        if (c1 >= 0) compute_page(kb[b + 1], c1);
+        // the other pair of buffers held the previous pair, done by every
+        // wave before the last barrier
+        const int nb = 2 - b;
+        if (n0 >= 0) store_page(pv[0], kb[nb]);
+        if (n1 >= 0) store_page(pv[1], kb[nb + 1]);
+        const int a0 = next_live(), a1 = next_live();
+        if (a0 >= 0) load_page(a0, pv[0]);
+        if (a1 >= 0) load_page(a1, pv[1]);
         __syncthreads();
-        cur = nxt;
-        nxt = after;
+        c0 = n0; c1 = n1;
+        n0 = a0; n1 = a1;
     }
     for (int idx = tid; idx < (tq1 - tq0) * npg; idx += NT) {
         const int qq = idx / npg, pi = idx % npg;
