@@ -214,14 +214,14 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
 //
 // Each live page is read once per workgroup with coalesced 16-byte loads
 // (every thread a 32-byte slice of a key row), decoded FP8 -> bf16 once and
-// stored to one of two bf16 page buffers in LDS, from which all 8 waves read
-// their A operands ready to use: the decode costs 16 VALU instructions per
-// wave and page instead of one per MFMA, and VALU issue does not overlap MFMA
-// issue well on a SIMD.  The next page's slice is loaded into registers while
-// the current page is multiplied, decoded and stored after it; pages go
-// through LDS two at a time (four bf16 page buffers, one barrier per pair).  Pages that every token sees whole skip the causal mask.  The
-// running block max per (query, block) is staged in LDS and written out
-// coalesced at the end.
+// stored to a bf16 page buffer in LDS, from which all 8 waves read their A
+// operands ready to use: the decode costs 16 VALU instructions per wave and
+// page instead of one per MFMA, and VALU issue does not overlap MFMA issue
+// well on a SIMD.  Pages go through LDS two at a time (four page buffers, one
+// barrier per pair); the next pair's slices are loaded into registers while
+// the current pair is multiplied, and decoded and stored after it.  Pages
+// that every token sees whole skip the causal mask.  The running block max
+// per (query, block) is staged in LDS and written out coalesced at the end.
 
 constexpr int kPWaves = 8;        // waves per workgroup, two per SIMD
 constexpr int kPMaxPC = 8;        // blocks per workgroup, at most
