@@ -106,6 +106,33 @@ def test_prefill_score_select(msa):
     check_topk_end_to_end(gt, np.where(np.isnan(ref), -np.inf, ref), rows=rows)
 
 
+def test_prefill_noncausal_reading(msa):
+    """The other reading of the prefill key set: every query token sees exactly
+    the 8192-token context, no causal mask.  It fits the same calls as one row
+    per query token (R = 8192, T = 1, seq_len 8192), each row carrying its
+    request's block table; scores and selection are checked on sampled rows."""
+    import dataclasses
+    base = synth.prefill()
+    R0, T0 = base.R, base.T
+    MB = 8192 // base.B
+    bt = base.block_table[:, :MB].repeat_interleave(T0, dim=0).contiguous()      # [8192, 64]
+    c = dataclasses.replace(base, name="prefill_noncausal", R=R0 * T0, T=1, MB=MB, block_table=bt,
+                            seq_lens=torch.full((R0 * T0,), 8192, dtype=torch.int32))
+    _say(f"case {c.name}")
+    d = upload(c)
+    scores = run_score(msa, c, d)
+    topk = run_select(msa, c, scores)
+    torch.cuda.synchronize()
+    gs, gt = scores.cpu().numpy(), topk.cpu().numpy()
+    check_topk_isolated(gt, gs)
+    rows = sorted(set(list(range(0, 40)) + list(range(2040, 2060)) + list(range(8150, 8192))))
+    ref = np.full_like(gs, np.nan, dtype=np.float64)
+    for a, b in ((0, 40), (2040, 2060), (8150, 8192)):
+        ref[a:b] = oracle_scores(c, n_range=(a, b), threads=16)[a:b]
+    check_scores(gs, ref, rows=rows)
+    check_topk_end_to_end(gt, np.where(np.isnan(ref), -np.inf, ref), rows=rows)
+
+
 @pytest.mark.parametrize("k", [8, 16, 32, 128])
 def test_hbm_decode(msa, k):
     c = synth.hbm_decode(k)
