@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 # the launch msa_select_sparse_decode makes at this shape
-ROOFLINE_KERNEL = "attn_token_select_kernel<128>"
+ROOFLINE_KERNEL = "attn_token_select_kernel<128, 2>"
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -249,7 +249,7 @@ def bf16_kv_attention(torch, msa, case, topk, copies: int = 4, reps: int = 50) -
     gbs = nbytes / t / 1e9
     return {"workload": "msa_sparse_decode, 16 rows x 4 tokens, 16384 ctx, top-k 16, dense bf16 K/V caches",
             "us": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
-            "roofline": {"bound": "hbm", "kernel": "attn_token_kernel<128, bf16>", "achieved": round(gbs, 1),
+            "roofline": {"bound": "hbm", "kernel": "attn_token_kernel<128, 1>", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
