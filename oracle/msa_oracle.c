@@ -193,6 +193,121 @@ int orc_select_topk(const double *scores, int64_t N, int64_t MB, int64_t k, int3
     return ORC_OK;
 }
 
+/* -------------------------------------------------- prefill score + select */
+
+/*
+ * Score-to-selection over a ragged prefill batch, one call per batch
+ * (Cacheon "Kernel ABI", "Attention block slots",
+ * attention.msa_prefill_block_score).  Readings where the page is silent:
+ *  - request b (block_table row slot_ids[b]) has new query tokens
+ *    q[cu_seqlens[b] .. cu_seqlens[b+1]); its query block qb (block_size_q
+ *    tokens, the last one possibly short) sees the keys
+ *    [0, V) with V = min(seq_lens[b], prefix_lens[b] + qb * block_size_q),
+ *    the keys before the block's first token;
+ *  - score(h, qb, j) = scale * max over the block's tokens t and the visible
+ *    keys s of block j of sum_d q[t][h][d] * code(index_k[page(j)][s][d]);
+ *    the candidates are the blocks j < ceil(V / B);
+ *  - forced blocks: the first init_blocks and the last local_blocks
+ *    candidates; the selection takes the forced blocks (lower ids first when
+ *    they exceed topk), then the highest-scoring other candidates (ties to
+ *    the lower id, -0 equal to +0), emits ascending ids, pads with -1;
+ *  - out_topk [Hq, all_qb, topk] row cu_seqblocks_q[b] + qb; rows no query
+ *    block owns hold -1.
+ * scores, when not NULL, receives [Hq, all_qb, MB] (-inf where no candidate).
+ */
+int orc_prefill_select(const void *q, int q_dtype, int64_t total_q, int64_t Hq, int64_t Di,
+                       const void *index_k, int k_dtype, int64_t P, int64_t B,
+                       const int32_t *block_table, int64_t nslots, int64_t MB,
+                       const int32_t *slot_ids, const int32_t *cu_seqlens, const int32_t *seq_lens,
+                       const int32_t *prefix_lens, int64_t batch, int64_t bsq, int64_t topk,
+                       int64_t init_blocks, int64_t local_blocks, double scale,
+                       const int32_t *cu_seqblocks_q, int64_t all_qb, int64_t h_begin, int64_t h_end,
+                       int32_t *out_topk, double *scores)
+{
+    if (Hq < 1 || Di < 1 || B < 1 || MB < 1 || bsq < 1 || topk < 1 || init_blocks < 0 ||
+        local_blocks < 0 || !(scale > 0) || h_begin < 0 || h_end > Hq || batch < 0)
+        return ORC_EARG;
+    for (int64_t i = 0; i < Hq * all_qb * topk; i++)
+        if (i / (all_qb * topk) >= h_begin && i / (all_qb * topk) < h_end)
+            out_topk[i] = -1;
+    if (scores)
+        for (int64_t i = h_begin * all_qb * MB; i < h_end * all_qb * MB; i++)
+            scores[i] = -INFINITY;
+    cand_t *c = malloc(sizeof(cand_t) * (size_t)MB);
+    int32_t *ids = malloc(sizeof(int32_t) * (size_t)MB);
+    double *sc = malloc(sizeof(double) * (size_t)MB);
+    char *forced = malloc((size_t)MB);
+    if (!c || !ids || !sc || !forced) { free(c); free(ids); free(sc); free(forced); return ORC_EARG; }
+    int rc = ORC_OK;
+    for (int64_t b = 0; b < batch && rc == ORC_OK; b++) {
+        const int64_t q0 = cu_seqlens[b], nq = (int64_t)cu_seqlens[b + 1] - q0;
+        const int64_t nqb = (nq + bsq - 1) / bsq;
+        const int64_t row0 = cu_seqblocks_q[b];
+        const int64_t slot = slot_ids[b];
+        if (nq < 0 || q0 < 0 || q0 + nq > total_q || slot < 0 || slot >= nslots ||
+            (int64_t)cu_seqblocks_q[b + 1] - row0 != nqb || row0 < 0 || row0 + nqb > all_qb ||
+            prefix_lens[b] < 0 || seq_lens[b] < 0 || (int64_t)seq_lens[b] > MB * B) {
+            rc = ORC_EARG;
+            break;
+        }
+        for (int64_t h = h_begin; h < h_end && rc == ORC_OK; h++) {
+            for (int64_t qb = 0; qb < nqb && rc == ORC_OK; qb++) {
+                int64_t V = (int64_t)prefix_lens[b] + qb * bsq;
+                if (V > seq_lens[b])
+                    V = seq_lens[b];
+                const int64_t ncand = (V + B - 1) / B;
+                const int64_t t1 = (qb + 1) * bsq < nq ? (qb + 1) * bsq : nq;
+                for (int64_t j = 0; j < ncand; j++) {
+                    const int64_t page = block_table[slot * MB + j];
+                    if (page < 0 || page >= P) { rc = ORC_EPAGE; break; }
+                    const int64_t s1 = (j + 1) * B < V ? (j + 1) * B : V;
+                    double best = -INFINITY;
+                    for (int64_t t = qb * bsq; t < t1; t++)
+                        for (int64_t s = j * B; s < s1; s++) {
+                            double dot = 0.0;
+                            for (int64_t d = 0; d < Di; d++)
+                                dot += elem(q, q_dtype, ((q0 + t) * Hq + h) * Di + d) *
+                                       elem(index_k, k_dtype, (page * B + (s - j * B)) * Di + d);
+                            if (isnan(dot)) rc = ORC_ENAN;
+                            if (dot > best) best = dot;
+                        }
+                    sc[j] = scale * best;
+                    if (scores)
+                        scores[(h * all_qb + row0 + qb) * MB + j] = sc[j];
+                }
+                if (rc != ORC_OK)
+                    break;
+                /* forced blocks first (lower ids first), then by score */
+                int64_t take = 0;
+                for (int64_t j = 0; j < ncand; j++)
+                    forced[j] = (j < init_blocks) || (j >= ncand - local_blocks);
+                for (int64_t j = 0; j < ncand && take < topk; j++)
+                    if (forced[j])
+                        ids[take++] = (int32_t)j;
+                int64_t nc = 0;
+                for (int64_t j = 0; j < ncand; j++)
+                    if (!forced[j]) {
+                        c[nc].s = (sc[j] == 0.0) ? 0.0 : sc[j];
+                        c[nc].j = (int32_t)j;
+                        nc++;
+                    }
+                qsort(c, (size_t)nc, sizeof(cand_t), by_score_then_id);
+                for (int64_t i = 0; i < nc && take < topk; i++)
+                    ids[take++] = c[i].j;
+                qsort(ids, (size_t)take, sizeof(int32_t), by_id);
+                int32_t *dst = out_topk + (h * all_qb + row0 + qb) * topk;
+                for (int64_t i = 0; i < topk; i++)
+                    dst[i] = i < take ? ids[i] : -1;
+            }
+        }
+    }
+    free(c);
+    free(ids);
+    free(sc);
+    free(forced);
+    return rc;
+}
+
 /* --------------------------------------------------------------- attention */
 
 /*

@@ -34,6 +34,7 @@ E4M3_NAN_CODE = 0x7F
 
 _TENSOR_IDS = {
     "q_idx": 1, "index": 2, "q": 3, "k": 4, "v": 5, "perm": 6, "lens": 7, "topk": 8,
+    "slots": 9,
 }
 
 
@@ -252,3 +253,113 @@ def random_topk(case: Case, seed: int = 11) -> torch.Tensor:
         if m:
             out[n, :m] = np.sort(g.choice(nvis, size=m, replace=False))
     return torch.from_numpy(out)
+
+
+# ------------------------------------------------- ragged prefill (score + select)
+
+@dataclasses.dataclass
+class PrefillBatch:
+    """A ragged prefill batch for the fused score-to-selection call
+    (attention.msa_prefill_block_score in Cacheon "Kernel ABI").  Request b
+    (block-table row slot_ids[b]) has new tokens q[cu_seqlens[b] ..
+    cu_seqlens[b+1]) after prefix_lens[b] cached keys; seq_lens[b] =
+    prefix_lens[b] + its new tokens.
+
+    q [total_q, Hq, Di] (bf16 or f32), index_k [P, B, Di] (E4M3 codes or f32),
+    block_table [slots, MB] i32, the int32 vectors, and the selection policy."""
+    name: str
+    Hq: int
+    Di: int
+    B: int
+    P: int
+    MB: int
+    block_size_q: int
+    topk: int
+    init_blocks: int
+    local_blocks: int
+    scale: float
+    q: torch.Tensor
+    index_k: torch.Tensor
+    block_table: torch.Tensor
+    slot_ids: torch.Tensor
+    cu_seqlens: torch.Tensor
+    seq_lens: torch.Tensor
+    prefix_lens: torch.Tensor
+    cu_seqblocks_q: torch.Tensor
+    all_qb: int
+    fp8: bool = True
+
+    @property
+    def batch(self) -> int:
+        return int(self.slot_ids.shape[0])
+
+    @property
+    def total_q(self) -> int:
+        return int(self.q.shape[0])
+
+
+def prefill_batch(name: str, *, new_tokens: Sequence[int], prefix: Sequence[int], Hq: int, Di: int,
+                  block_size_q: int, topk: int, init_blocks: int = 0, local_blocks: int = 0,
+                  slots: Optional[int] = None, P: Optional[int] = None, MB: Optional[int] = None,
+                  extra_qb_rows: int = 0, fp8: bool = True, seed: int = 0,
+                  B: int = BLOCK) -> PrefillBatch:
+    """Random ragged prefill batch.  Requests take disjoint random pages of the
+    pool and random block-table rows (slot ids); unused pages, tail slots and
+    table entries past a request's last block are poisoned.  ``extra_qb_rows``
+    output rows past the last request's query blocks belong to no request."""
+    nq = np.asarray(new_tokens, dtype=np.int64)
+    pre = np.asarray(prefix, dtype=np.int64)
+    lens = nq + pre
+    batch = len(nq)
+    nblk = (lens + B - 1) // B
+    MB = int(max(1, nblk.max())) if MB is None else MB
+    assert nblk.max() <= MB
+    slots = batch + 2 if slots is None else slots
+    P = int(nblk.sum()) + 3 if P is None else P
+    assert int(nblk.sum()) < P
+    g = _rng(seed, "perm")
+    perm = g.permutation(P).astype(np.int32)
+    poison_page = int(perm[int(nblk.sum())])
+    slot_ids = _rng(seed, "slots").permutation(slots)[:batch].astype(np.int32)
+    bt = np.full((slots, MB), poison_page, dtype=np.int32)
+    slot_valid = np.zeros((P, B), dtype=bool)
+    off = 0
+    for b in range(batch):
+        pages = perm[off: off + nblk[b]]
+        off += nblk[b]
+        bt[slot_ids[b], : nblk[b]] = pages
+        for j, pg in enumerate(pages):
+            slot_valid[pg, : min(B, int(lens[b]) - j * B)] = True
+    vals = _rng(seed, "index").standard_normal((P, B, Di), dtype=np.float32)
+    if fp8:
+        codes, scale = quantize_e4m3(vals[slot_valid])
+        index_k = torch.full((P, B, Di), E4M3_NAN_CODE, dtype=torch.uint8)
+        index_k[torch.from_numpy(slot_valid)] = codes
+    else:
+        scale = 1.0
+        index_k = torch.from_numpy(vals)
+        index_k[torch.from_numpy(~slot_valid)] = float("nan")
+    total_q = int(nq.sum())
+    qv = _rng(seed, "q_idx").standard_normal((total_q, Hq, Di), dtype=np.float32)
+    q = to_bf16(qv) if fp8 else torch.from_numpy(qv)
+    cu = np.concatenate([[0], np.cumsum(nq)]).astype(np.int32)
+    nqb = (nq + block_size_q - 1) // block_size_q
+    cuqb = np.concatenate([[0], np.cumsum(nqb)]).astype(np.int32)
+    return PrefillBatch(name=name, Hq=Hq, Di=Di, B=B, P=P, MB=MB, block_size_q=block_size_q,
+                        topk=topk, init_blocks=init_blocks, local_blocks=local_blocks,
+                        scale=scale, q=q, index_k=index_k, block_table=torch.from_numpy(bt),
+                        slot_ids=torch.from_numpy(slot_ids), cu_seqlens=torch.from_numpy(cu),
+                        seq_lens=torch.from_numpy(lens.astype(np.int32)),
+                        prefix_lens=torch.from_numpy(pre.astype(np.int32)),
+                        cu_seqblocks_q=torch.from_numpy(cuqb), all_qb=int(cuqb[-1]) + extra_qb_rows,
+                        fp8=fp8)
+
+
+def prefill_ragged(seed: int = 4100) -> PrefillBatch:
+    """The fused prefill score-to-selection workload: 4 requests with 2048,
+    1536, 1024 and 512 new tokens over prefixes of 8192, 4096, 12288 and 2048
+    tokens (up to 13824 keys, 108 blocks), 4 index query heads, Di = 128,
+    query blocks of 64 tokens, top-k 16 with 1 initial and 2 local blocks."""
+    return prefill_batch("prefill_ragged_4req", new_tokens=[2048, 1536, 1024, 512],
+                         prefix=[8192, 4096, 12288, 2048], Hq=4, Di=128, block_size_q=64, topk=16,
+                         init_blocks=1, local_blocks=2, P=512, seed=seed)

@@ -426,3 +426,109 @@ def test_round_bf16_matches_torch(orc):
     assert np.array_equal(orc.round_bf16(x32), ref)
     m = x32[:6000].reshape(60, 100)
     assert np.array_equal(orc.round_bf16(m.T), ref[:6000].reshape(60, 100).T)   # strided input
+
+
+# ------------------------------------------- ragged prefill score + select
+
+def _pb_dense_keys(pb, b):
+    """Request b's keys in position order, decoded, [L, Di]."""
+    arr = _decode(pb.index_k)
+    L = int(pb.seq_lens[b])
+    pages = pb.block_table[int(pb.slot_ids[b])].numpy()
+    idx = np.arange(L)
+    return arr[pages[idx // pb.B], idx % pb.B]
+
+
+def brute_prefill_select(pb):
+    """Dense numpy route: per (head, query block) a masked [block tokens x keys]
+    dot matrix, block maxima by reshaping, then the forced-then-by-score rule."""
+    q = _decode(pb.q)
+    out = np.full((pb.Hq, pb.all_qb, pb.topk), -1, dtype=np.int32)
+    for b in range(pb.batch):
+        q0, q1 = int(pb.cu_seqlens[b]), int(pb.cu_seqlens[b + 1])
+        nq = q1 - q0
+        K = _pb_dense_keys(pb, b)
+        for qb in range((nq + pb.block_size_q - 1) // pb.block_size_q):
+            V = min(int(pb.seq_lens[b]), int(pb.prefix_lens[b]) + qb * pb.block_size_q)
+            ncand = -(-V // pb.B)
+            t0, t1 = q0 + qb * pb.block_size_q, min(q1, q0 + (qb + 1) * pb.block_size_q)
+            for h in range(pb.Hq):
+                dots = q[t0:t1, h] @ K[:V].T                                  # [tokens, V]
+                pad = ncand * pb.B - V
+                dots = np.concatenate([dots, np.full((t1 - t0, pad), -np.inf)], axis=1)
+                sc = pb.scale * dots.reshape(t1 - t0, ncand, pb.B).max(axis=(0, 2))
+                forced = [j for j in range(ncand) if j < pb.init_blocks or j >= ncand - pb.local_blocks]
+                chosen = forced[:pb.topk]
+                rest = sorted((j for j in range(ncand) if j not in forced), key=lambda j: (-sc[j], j))
+                chosen += rest[:pb.topk - len(chosen)]
+                chosen = sorted(chosen)
+                out[h, int(pb.cu_seqblocks_q[b]) + qb, :len(chosen)] = chosen
+    return out
+
+
+def _tiny_batches():
+    return [
+        synth.prefill_batch("pb_fp8", new_tokens=[5, 3, 8], prefix=[6, 0, 11], Hq=2, Di=4,
+                            block_size_q=3, topk=3, init_blocks=1, local_blocks=1, B=4, seed=11,
+                            extra_qb_rows=2),
+        synth.prefill_batch("pb_f32", new_tokens=[9, 1], prefix=[30, 2], Hq=3, Di=8,
+                            block_size_q=4, topk=4, init_blocks=0, local_blocks=2, B=4, seed=12,
+                            fp8=False),
+        synth.prefill_batch("pb_bsq1", new_tokens=[6, 4], prefix=[17, 9], Hq=1, Di=4,
+                            block_size_q=1, topk=2, B=4, seed=13),
+    ]
+
+
+@pytest.mark.parametrize("pb", _tiny_batches(), ids=lambda p: p.name)
+def test_prefill_select_matches_brute_force(orc, pb):
+    got, sc = orc.prefill_select(pb.q, pb.index_k, pb.block_table, pb.slot_ids, pb.cu_seqlens,
+                                 pb.seq_lens, pb.prefix_lens, pb.block_size_q, pb.topk,
+                                 pb.init_blocks, pb.local_blocks, pb.scale, pb.cu_seqblocks_q,
+                                 pb.all_qb, return_scores=True)
+    assert np.array_equal(got, brute_prefill_select(pb))
+    assert (got[:, int(pb.cu_seqblocks_q[-1]):] == -1).all()      # rows no query block owns
+
+
+def test_prefill_select_one_token_blocks_equal_per_token_path(orc):
+    """1-token query blocks, one head, no forced blocks: the per-token score and
+    select of the decode rows whose visibility is the same key range (a decode
+    token sees its own key, a query block only the keys before it: seq_len =
+    prefix + T - 1), through the independent per-token oracle functions."""
+    T, R = 6, 3
+    pb = synth.prefill_batch("pb_eq", new_tokens=[T] * R, prefix=[40, 3, 77], Hq=1, Di=8,
+                             block_size_q=1, topk=4, B=8, seed=14)
+    got = orc.prefill_select(pb.q, pb.index_k, pb.block_table, pb.slot_ids, pb.cu_seqlens,
+                             pb.seq_lens, pb.prefix_lens, 1, pb.topk, 0, 0, pb.scale,
+                             pb.cu_seqblocks_q, pb.all_qb)[0]
+    bt = pb.block_table[pb.slot_ids.long()].contiguous()
+    lens = (pb.prefix_lens + T - 1).to(torch.int32)
+    scores = orc.block_score(pb.q[:, 0, :].contiguous(), pb.index_k, bt, lens, T, pb.scale)
+    ref = orc.select_topk(scores, pb.topk)
+    assert np.array_equal(got, ref)
+
+
+def test_prefill_select_forced_blocks(orc):
+    """topk <= forced blocks: exactly the forced blocks, lower ids first;
+    topk >= candidates: every candidate."""
+    base = dict(new_tokens=[8, 5], prefix=[33, 21], Hq=2, Di=4, block_size_q=2, B=4, seed=15)
+    pb = synth.prefill_batch("pb_forced", topk=3, init_blocks=2, local_blocks=3, **base)
+    got = orc.prefill_select(pb.q, pb.index_k, pb.block_table, pb.slot_ids, pb.cu_seqlens,
+                             pb.seq_lens, pb.prefix_lens, pb.block_size_q, pb.topk, pb.init_blocks,
+                             pb.local_blocks, pb.scale, pb.cu_seqblocks_q, pb.all_qb)
+    for b in range(pb.batch):
+        for qb in range(int(pb.cu_seqblocks_q[b + 1] - pb.cu_seqblocks_q[b])):
+            V = min(int(pb.seq_lens[b]), int(pb.prefix_lens[b]) + qb * pb.block_size_q)
+            ncand = -(-V // pb.B)
+            forced = sorted({j for j in range(ncand) if j < 2 or j >= ncand - 3})[:3]
+            for h in range(pb.Hq):
+                row = got[h, int(pb.cu_seqblocks_q[b]) + qb]
+                assert list(row[row >= 0]) == forced
+    pb = synth.prefill_batch("pb_all", topk=40, init_blocks=1, local_blocks=1, **base)
+    got = orc.prefill_select(pb.q, pb.index_k, pb.block_table, pb.slot_ids, pb.cu_seqlens,
+                             pb.seq_lens, pb.prefix_lens, pb.block_size_q, pb.topk, pb.init_blocks,
+                             pb.local_blocks, pb.scale, pb.cu_seqblocks_q, pb.all_qb)
+    for b in range(pb.batch):
+        for qb in range(int(pb.cu_seqblocks_q[b + 1] - pb.cu_seqblocks_q[b])):
+            V = min(int(pb.seq_lens[b]), int(pb.prefix_lens[b]) + qb * pb.block_size_q)
+            row = got[0, int(pb.cu_seqblocks_q[b]) + qb]
+            assert list(row[row >= 0]) == list(range(-(-V // pb.B)))

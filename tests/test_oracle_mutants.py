@@ -31,6 +31,12 @@ MUTANTS = [
     ("e4m3_wrong_bias", "v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);", 0),
     ("e4m3_wrong_subnormal", "v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);", 0),
     ("bf16_wrong_half", "uint32_t u = (uint32_t)bits << 16;", "uint32_t u = (uint32_t)bits << 15;", 0),
+    ("prefill_sees_own_block", "int64_t V = (int64_t)prefix_lens[b] + qb * bsq;", "int64_t V = (int64_t)prefix_lens[b] + (qb + 1) * bsq;", 0),
+    ("prefill_block_max_first_token", "for (int64_t t = qb * bsq; t < t1; t++)", "for (int64_t t = qb * bsq; t < qb * bsq + 1; t++)", 0),
+    ("prefill_wrong_head", "elem(q, q_dtype, ((q0 + t) * Hq + h) * Di + d)", "elem(q, q_dtype, ((q0 + t) * Hq) * Di + d)", 0),
+    ("prefill_local_off_by_one", "forced[j] = (j < init_blocks) || (j >= ncand - local_blocks);", "forced[j] = (j < init_blocks) || (j > ncand - local_blocks);", 0),
+    ("prefill_drops_init", "forced[j] = (j < init_blocks) || (j >= ncand - local_blocks);", "forced[j] = (j >= ncand - local_blocks);", 0),
+    ("prefill_ignores_slot", "const int64_t page = block_table[slot * MB + j];", "const int64_t page = block_table[b * MB + j];", 0),
 ]
 
 
