@@ -206,6 +206,70 @@ def prefill_score(torch, msa, synth, copies: int = 4, reps: int = 50) -> dict:
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
 
 
+def prefill_select_ragged(torch, msa, synth, copies: int = 4, reps: int = 50) -> dict:
+    """msa_prefill_block_score on the ragged prefill batch (4 requests with
+    2048/1536/1024/512 new tokens over 8192/4096/12288/2048 cached, 4 index
+    heads, Di = 128, 64-token query blocks, top-16 with 1 initial and 2 local
+    blocks): plan, scoring and selection launches, timed together on cold
+    index-pool copies."""
+    pb = synth.prefill_ragged()
+    dev = "cuda"
+    q = pb.q.to(dev)
+    idx0 = pb.index_k.view(torch.float8_e4m3fn).to(dev)
+    pools = [idx0] + [idx0.clone() for _ in range(copies - 1)]
+    ints = {n: getattr(pb, n).to(dev) for n in ("block_table", "slot_ids", "cu_seqlens", "seq_lens",
+                                               "prefix_lens", "cu_seqblocks_q")}
+    out = [torch.full((pb.Hq, pb.all_qb, pb.topk), -1, dtype=torch.int32, device=dev)
+           for _ in range(copies)]
+    nbytes = msa.msa_prefill_block_score_workspace_bytes(pb.batch, pb.Hq, pb.all_qb, pb.MB,
+                                                         pb.block_size_q)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def body():
+        for i in range(copies):
+            msa.msa_prefill_block_score(q, pools[i], ints["block_table"], ints["slot_ids"],
+                                        ints["cu_seqlens"], ints["seq_lens"], ints["prefix_lens"],
+                                        pb.block_size_q, pb.B, pb.topk, pb.init_blocks,
+                                        pb.local_blocks, pb.scale, ints["cu_seqblocks_q"], out[i], ws)
+    with torch.cuda.stream(stream):
+        body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / 1000.0 / (reps * copies)
+    # dot products: every (head, query-block token, visible key) triple
+    cu = pb.cu_seqlens.numpy().astype(np.int64)
+    dots = 0
+    for b in range(pb.batch):
+        nq = int(cu[b + 1] - cu[b])
+        for qb in range(-(-nq // pb.block_size_q)):
+            ntok = min(pb.block_size_q, nq - qb * pb.block_size_q)
+            V = min(int(pb.seq_lens[b]), int(pb.prefix_lens[b]) + qb * pb.block_size_q)
+            dots += ntok * V
+    flops = 2 * dots * pb.Di * pb.Hq
+    tflops = flops / t / 1e12
+    return {"workload": "ragged prefill score-to-selection: 4 requests, 2048/1536/1024/512 new tokens "
+                        "over 8192/4096/12288/2048 cached, 4 heads, Di=128, 64-token query blocks, "
+                        "top-16 (1 initial + 2 local blocks)",
+            "call_us": round(t * 1e6, 3), "algorithmic_gflop": round(flops / 1e9, 3),
+            "roofline": {"bound": "mfma", "kernel": "msa_prefill_block_score (plan + scoring + select)",
+                         "achieved": round(tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)}}
+
+
 def bf16_kv_attention(torch, msa, case, topk, copies: int = 4, reps: int = 50) -> dict:
     """msa_sparse_decode over the same selection with the caches held as dense
     bf16 (attention.decode's commissioned cache; the FP8 values widened
@@ -430,6 +494,7 @@ def main():
     }
     if not a.no_prefill:
         res["prefill_score"] = prefill_score(torch, msa, synth)
+        res["prefill_select_ragged"] = prefill_select_ragged(torch, msa, synth)
     if not a.no_variants:
         del pools, scores, out, ws
         res["bf16_kv_attention"] = bf16_kv_attention(torch, msa, case, tk_host)

@@ -18,6 +18,9 @@ There is no CPU fallback: importing fails when the library is missing.
     msa_decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
                     tokens_per_row, k, block_size, idx_scale, sm_scale, k_scale,
                     v_scale, scores, topk_idx, out, workspace)
+    msa_prefill_block_score(q, index_k, block_table, slot_ids, cu_seqlens, seq_lens,
+                            prefix_lens, block_size_q, block_size_k, topk, init_blocks,
+                            local_blocks, scale, cu_seqblocks_q, out_topk, workspace)
 
 Each call writes into the outputs given (same argument order as the C ABI)
 and returns None; a rejected call raises MsaError and leaves the outputs as
@@ -44,7 +47,7 @@ _DTYPES = {
 }
 EXPORTS = ("msa_block_score", "msa_select_topk", "msa_sparse_decode_workspace_bytes",
            "msa_sparse_decode", "msa_select_sparse_decode", "msa_decode_step_workspace_bytes",
-           "msa_decode_step",
+           "msa_decode_step", "msa_prefill_block_score_workspace_bytes", "msa_prefill_block_score",
            "msa_get_last_error", "msa_error_string")
 
 
@@ -82,6 +85,11 @@ def _load() -> ctypes.CDLL:
     lib.msa_decode_step.restype = None
     lib.msa_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, f32, f32, f32, f32, P, P, P,
                                     vp, sz, vp]
+    lib.msa_prefill_block_score_workspace_bytes.restype = sz
+    lib.msa_prefill_block_score_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.msa_prefill_block_score.restype = None
+    lib.msa_prefill_block_score.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, i32, i32, f32, P, P,
+                                            vp, sz, vp]
     lib.msa_get_last_error.restype = i32
     lib.msa_get_last_error.argtypes = []
     lib.msa_error_string.restype = ctypes.c_char_p
@@ -184,4 +192,25 @@ def msa_decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
                         int(block_size), float(idx_scale), float(sm_scale), float(k_scale),
                         float(v_scale), *(ctypes.byref(x) for x in d[7:]), ws_ptr, ws_bytes,
                         _stream(stream))
+    _check()
+
+
+def msa_prefill_block_score_workspace_bytes(batch: int, num_q_heads: int, all_seqblock_q: int,
+                                            max_blocks: int, block_size_q: int) -> int:
+    return int(lib.msa_prefill_block_score_workspace_bytes(batch, num_q_heads, all_seqblock_q,
+                                                           max_blocks, block_size_q))
+
+
+def msa_prefill_block_score(q, index_k, block_table, slot_ids, cu_seqlens, seq_lens, prefix_lens,
+                            block_size_q: int, block_size_k: int, topk: int, init_blocks: int,
+                            local_blocks: int, scale: float, cu_seqblocks_q, out_topk, workspace,
+                            stream=None) -> None:
+    d = [tensor_desc(t) for t in (q, index_k, block_table, slot_ids, cu_seqlens, seq_lens,
+                                  prefix_lens, cu_seqblocks_q, out_topk)]
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    lib.msa_prefill_block_score(*(ctypes.byref(x) for x in d[:7]), int(block_size_q),
+                                int(block_size_k), int(topk), int(init_blocks), int(local_blocks),
+                                float(scale), ctypes.byref(d[7]), ctypes.byref(d[8]), ws_ptr,
+                                ws_bytes, _stream(stream))
     _check()

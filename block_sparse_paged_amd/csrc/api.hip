@@ -284,6 +284,86 @@ int32_t run_select_attn(const TopkParams &tk, AttnParams &at, const AttnPlan &pl
     return run_attn(at, plan, qt, kvt, D, stream);
 }
 
+// Validates the ragged prefill arguments and fills p except the workspace.
+int32_t prep_prefill(const msa_tensor *q, const msa_tensor *index_k, const msa_tensor *block_table,
+                     const msa_tensor *slot_ids, const msa_tensor *cu_seqlens, const msa_tensor *seq_lens,
+                     const msa_tensor *prefix_lens, int32_t block_size_q, int32_t block_size_k, int32_t topk,
+                     int32_t init_blocks, int32_t local_blocks, float scale,
+                     const msa_tensor *cu_seqblocks_q, msa_tensor *out_topk, PrefillSelParams &p, int &Di) {
+    Check c;
+    desc(c, q, 3);
+    desc(c, index_k, 3);
+    desc(c, block_table, 2);
+    desc(c, slot_ids, 1);
+    desc(c, cu_seqlens, 1);
+    desc(c, seq_lens, 1);
+    desc(c, prefix_lens, 1);
+    desc(c, cu_seqblocks_q, 1);
+    desc(c, out_topk, 3);
+    dtype_in(c, q, {MSA_BF16});
+    dtype_in(c, index_k, {MSA_FP8_E4M3FN});
+    for (const msa_tensor *t : {block_table, slot_ids, cu_seqlens, seq_lens, prefix_lens, cu_seqblocks_q,
+                                (const msa_tensor *)out_topk})
+        dtype_in(c, t, {MSA_I32});
+    if (!c.ok()) return c.err;
+    const int64_t total_q = q->shape[0], Hq = q->shape[1];
+    Di = (int)q->shape[2];
+    const int64_t P = index_k->shape[0], nslots = block_table->shape[0], MB = block_table->shape[1];
+    const int64_t batch = slot_ids->shape[0], all_qb = out_topk->shape[1];
+    if (seq_lens->shape[0] != batch || prefix_lens->shape[0] != batch || cu_seqlens->shape[0] != batch + 1 ||
+        cu_seqblocks_q->shape[0] != batch + 1)
+        c.fail(MSA_ERR_SHAPE);
+    if (index_k->shape[1] != kBlock || index_k->shape[2] != Di) c.fail(MSA_ERR_SHAPE);
+    if (out_topk->shape[0] != Hq || out_topk->shape[2] != topk) c.fail(MSA_ERR_SHAPE);
+    if (Hq < 1) c.fail(MSA_ERR_SHAPE);
+    if (!c.ok()) return c.err;
+    if (Di != 64 && Di != 128) c.fail(MSA_ERR_UNSUPPORTED);
+    if (block_size_k != kBlock) c.fail(MSA_ERR_UNSUPPORTED);
+    if (MB < 1 || MB > kMaxMB) c.fail(MSA_ERR_UNSUPPORTED);
+    if (batch > kPlanMaxBatch) c.fail(MSA_ERR_UNSUPPORTED);
+    if (block_size_q < 1 || topk < 1 || init_blocks < 0 || local_blocks < 0) c.fail(MSA_ERR_ARG);
+    if (!(scale > 0.f) || !isfinite(scale)) c.fail(MSA_ERR_ARG);
+    if (!fits_i32(total_q) || !fits_i32(P) || !fits_i32(nslots) || !fits_i32(all_qb) ||
+        !fits_i32(Hq * all_qb))
+        c.fail(MSA_ERR_UNSUPPORTED);
+    if (!c.ok()) return c.err;
+    const PrefillGeom g = prefill_geom(batch, Hq, all_qb, MB, block_size_q);
+    if (g.Cmax > (1 << 28) || g.Umax > (1 << 28)) c.fail(MSA_ERR_UNSUPPORTED);
+    rows16(c, q);
+    rows16(c, index_k);
+    if (!c.ok()) return c.err;
+    p = PrefillSelParams{};
+    p.q = (const uint16_t *)q->data; p.q_st = q->stride[0]; p.q_sh = q->stride[1];
+    p.index_k = (const uint8_t *)index_k->data; p.k_sp = index_k->stride[0]; p.k_sb = index_k->stride[1];
+    p.bt = (const int32_t *)block_table->data; p.bt_sr = block_table->stride[0]; p.bt_sj = block_table->stride[1];
+    p.slot_ids = (const int32_t *)slot_ids->data; p.s_slot = slot_ids->stride[0];
+    p.cu_seqlens = (const int32_t *)cu_seqlens->data; p.s_cu = cu_seqlens->stride[0];
+    p.seq_lens = (const int32_t *)seq_lens->data; p.s_sl = seq_lens->stride[0];
+    p.prefix_lens = (const int32_t *)prefix_lens->data; p.s_pl = prefix_lens->stride[0];
+    p.cu_qb = (const int32_t *)cu_seqblocks_q->data; p.s_cq = cu_seqblocks_q->stride[0];
+    p.out = (int32_t *)out_topk->data;
+    p.o_sh = out_topk->stride[0]; p.o_sq = out_topk->stride[1]; p.o_si = out_topk->stride[2];
+    p.total_q = (int32_t)total_q; p.Hq = (int32_t)Hq; p.P = (int32_t)P; p.nslots = (int32_t)nslots;
+    p.MB = (int32_t)MB; p.batch = (int32_t)batch; p.bsq = block_size_q; p.topk = topk;
+    p.init_blocks = init_blocks; p.local_blocks = local_blocks; p.all_qb = (int32_t)all_qb;
+    p.scale = scale;
+    return MSA_OK;
+}
+
+// workgroups of the persistent prefill scoring launch: the current device's
+// CUs, a multiple of the 8 XCDs
+int32_t prefill_workgroups() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
+        cache[dev] = n / 8 * 8;
+    }
+    return cache[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -410,6 +490,36 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
     if (launch_score(sc, qit, kit, Di, stream) != hipSuccess) { set_error(MSA_ERR_LAUNCH); return; }
     const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);
     if (r != MSA_OK) set_error(r);
+}
+
+size_t msa_prefill_block_score_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t all_seqblock_q,
+                                               int32_t max_blocks, int32_t block_size_q) {
+    if (batch < 0 || num_q_heads < 1 || all_seqblock_q < 0 || max_blocks < 1 || block_size_q < 1) return 0;
+    return prefill_workspace_bytes(batch, num_q_heads, all_seqblock_q, max_blocks, block_size_q);
+}
+
+void msa_prefill_block_score(const msa_tensor *q, const msa_tensor *index_k, const msa_tensor *block_table,
+                             const msa_tensor *slot_ids, const msa_tensor *cu_seqlens,
+                             const msa_tensor *seq_lens, const msa_tensor *prefix_lens,
+                             int32_t block_size_q, int32_t block_size_k, int32_t topk, int32_t init_blocks,
+                             int32_t local_blocks, float scale, const msa_tensor *cu_seqblocks_q,
+                             msa_tensor *out_topk, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+    PrefillSelParams p;
+    int Di;
+    const int32_t e = prep_prefill(q, index_k, block_table, slot_ids, cu_seqlens, seq_lens, prefix_lens,
+                                   block_size_q, block_size_k, topk, init_blocks, local_blocks, scale,
+                                   cu_seqblocks_q, out_topk, p, Di);
+    if (e != MSA_OK) { set_error(e); return; }
+    if ((int64_t)p.Hq * p.all_qb == 0) return;
+    const size_t need = prefill_workspace_bytes(p.batch, p.Hq, p.all_qb, p.MB, p.bsq);
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) {
+        set_error(MSA_ERR_WORKSPACE);
+        return;
+    }
+    prefill_carve_workspace(workspace, p.batch, p.Hq, p.all_qb, p.MB, p.bsq, p);
+    p.nwg = prefill_workgroups();
+    if (launch_prefill_select(p, Di, stream) != hipSuccess) set_error(MSA_ERR_LAUNCH);
 }
 
 }  // extern "C"

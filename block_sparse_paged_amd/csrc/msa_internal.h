@@ -59,6 +59,49 @@ struct ReduceParams {
     float v_scale;
 };
 
+// Ragged prefill score-to-selection (msa_prefill_block_score).  Work is cut
+// into chunks of one request: up to kPrefillCols (token, query head) columns
+// covering whole query blocks of all heads (bsq*Hq <= kPrefillCols), whole
+// query blocks of a group of heads (bsq <= kPrefillCols), or a part of one
+// query block of one head; a chunk's blocks are cut into units of at most
+// kPMaxPC consecutive blocks, one unit per workgroup pass.
+constexpr int kPrefillCols = 512;            // columns of a chunk (one 8-wave tile of 4 MFMA column tiles)
+constexpr int kPlanMaxBatch = 8192;          // requests one call takes
+
+struct PrefillGeom {
+    int32_t hc;     // query heads per chunk
+    int32_t nqc;    // query blocks per chunk
+    int32_t NP;     // parts per query block (1 unless bsq > kPrefillCols)
+    int32_t HG;     // head groups: ceil(Hq / hc)
+    int64_t Cmax;   // chunks at most
+    int64_t Umax;   // units at most
+};
+
+struct PrefillSelParams {
+    const uint16_t *q; int64_t q_st, q_sh;             // [total_q, Hq, Di] bf16, inner stride 1
+    const uint8_t *index_k; int64_t k_sp, k_sb;        // [P, B, Di] FP8
+    const int32_t *bt; int64_t bt_sr, bt_sj;           // [nslots, MB]
+    const int32_t *slot_ids, *cu_seqlens, *seq_lens, *prefix_lens, *cu_qb;
+    int64_t s_slot, s_cu, s_sl, s_pl, s_cq;            // their strides
+    int32_t *out; int64_t o_sh, o_sq, o_si;            // [Hq, all_qb, topk]
+    int32_t total_q, Hq, P, nslots, MB, batch, bsq, topk, init_blocks, local_blocks, all_qb;
+    float scale;
+    PrefillGeom g;
+    int32_t nwg;                                       // workgroups of the scoring launch
+    // workspace (msa_prefill_block_score_workspace_bytes)
+    int32_t *hdr;       // [0] units, [1] blocks per unit, [2] chunks
+    int32_t *rowinfo;   // [all_qb]: request owning the query-block row, or -1
+    int4 *chunks;       // [Cmax][3] chunk descriptors
+    int4 *units;        // [Umax]: chunk, first block, blocks
+    float *ws;          // [Hq, all_qb, NP, MB] query-block maxima
+};
+
+PrefillGeom prefill_geom(int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq);
+size_t prefill_workspace_bytes(int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq);
+void prefill_carve_workspace(void *ws, int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq,
+                             PrefillSelParams &p);
+hipError_t launch_prefill_select(const PrefillSelParams &p, int Di, hipStream_t s);
+
 // Split partials in the workspace.  Split s of query token n leaves, per query
 // head h, its running max m (log2 units) and sum l as a pair, and its
 // unnormalised accumulator with the 8 consecutive d of group d/8 of all heads

@@ -1,0 +1,292 @@
+// One prefill score tile on MFMA: up to 512 query columns (bf16 rows of Di)
+// against a run of at most kPMaxPC consecutive logical blocks of one request's
+// FP8 index pages, reduced to the per-(column, block) maximum of the dot
+// products over the keys the column sees.  Shared by the prefill path of
+// msa_block_score (columns = query tokens of one row) and by the ragged
+// prefill score-to-selection call (columns = (token, query head) pairs of one
+// request), which differ only in which q row a column reads and how many keys
+// it sees.
+//
+// A workgroup of 8 waves (two per SIMD, one workgroup per CU) holds the tile.
+// The query rows are read coalesced and transposed into the MFMA operand
+// layout through LDS.  Each live page is read once per workgroup with
+// coalesced 16-byte loads (every thread a 32-byte slice of a key row),
+// decoded FP8 -> bf16 once and stored to a bf16 page buffer in LDS, from which
+// all 8 waves read their A operands ready to use: the decode costs 16 VALU
+// instructions per wave and page instead of one per MFMA, and VALU issue does
+// not overlap MFMA issue well on a SIMD.  Pages go through LDS two at a time
+// (four page buffers, one barrier per pair); the next pair's slices are loaded
+// into registers while the current pair is multiplied, and decoded and stored
+// after it.  Pages that every column sees whole skip the visibility mask.
+#pragma once
+
+#include "device_util.h"
+#include "msa_internal.h"
+
+namespace msa {
+
+constexpr int kPWaves = 8;        // waves per workgroup, two per SIMD
+constexpr int kPMaxPC = 8;        // blocks per tile, at most
+
+// max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
+// first, unlike fmaxf); the operands are dot products, never NaN (a NaN dot
+// product is outside the contract)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// bf16 A operands of the 16-key tile kt of the page in `buf`: key 16*kt +
+// lane%16; k-step ks covers d = 32*ks .. +31, lane group grp its d = 32*ks +
+// 8*grp .. +7: 16-byte unit 4*ks + grp of the key's bf16 row, stored
+// XOR-swizzled by the key.
+template <int DI>
+__device__ __forceinline__ void prefill_frag(const uint8_t *buf, int kt, int li, int grp, uint4 (&a)[DI / 32]) {
+    constexpr int KS = DI / 32, UPR = DI / 8;
+    const int key = kt * 16 + li;
+    const uint8_t *krow = buf + key * (DI * 2);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = *(const uint4 *)(krow + (((4 * ks + grp) ^ (key & (UPR - 1))) << 4));
+}
+
+// S^T tile of those keys against the wave's QT query tiles: acc[qt][e] =
+// q . k for key 16*kt + 4*grp + e and query column lane%16.
+template <int DI, int QT>
+__device__ __forceinline__ void prefill_mma(const uint4 (&a)[DI / 32], const uint4 (&qf)[QT][DI / 32],
+                                            f32x4 (&acc)[QT]) {
+    constexpr int KS = DI / 32;
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt)
+            acc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8, a[ks]), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
+}
+
+// LDS of one tile: two pairs of bf16 page buffers and the block maxima.
+template <int DI, int QT>
+struct PrefillLds {
+    static constexpr int PQ = 16 * QT * kPWaves;    // query columns
+    __attribute__((aligned(16))) uint8_t kb[4][kBlock * DI * 2];
+    float sbuf[PQ][kPMaxPC + 1];
+};
+
+// The pages of a tile: blocks j0 .. j0+npg-1 of a request whose block table
+// row is bt_row (nullptr: no valid row, every block's page is invalid).
+struct PrefillPages {
+    const uint8_t *index_k;
+    int64_t k_sp, k_sb;       // bytes per page, per key row
+    int P;
+    const int32_t *bt_row;
+    int64_t bt_sj;
+    int j0, npg;              // npg <= kPMaxPC
+    int vmin, vmax;           // keys seen by every column, by the column that sees most
+    float scale;
+};
+
+// Fills lds.sbuf[col][pi] (col < PQ, pi < npg) with scale * max over the keys
+// of block j0 + pi visible to column col of its dot products; -inf where the
+// column sees none of them, NaN where it sees some and the block's page id
+// lies outside [0, P) (the page is not read).  qrow(col) gives the column's bf16
+// query row (any valid address for columns that are not used), vis(col) the
+// number of keys the column sees (0 for unused columns).  Every thread of the
+// workgroup calls it; it ends with a barrier, after which sbuf is complete.
+template <int DI, int QT, class QRow, class Vis>
+__device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, Vis vis,
+                                             PrefillLds<DI, QT> &lds) {
+    constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
+    constexpr int NT = 64 * kPWaves;            // threads per workgroup
+    constexpr int RB = DI * 2;                  // bytes per bf16 row (query or key)
+    constexpr int UPR = DI / 8;                 // 16-byte units per bf16 row
+    constexpr int VPT = kBlock * DI / (16 * NT) > 0 ? kBlock * DI / (16 * NT) : 1;  // 16-byte FP8 loads per slice
+    constexpr int TPK = DI / (16 * VPT);        // slices per key row
+    constexpr int NLD = TPK * kBlock;           // threads holding a slice (whole waves)
+    constexpr int PQ = PrefillLds<DI, QT>::PQ;
+    static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
+    static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the first pair");
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = lane >> 4, li = lane & 15;
+    const int j0 = pg.j0, npg = pg.npg, vmin = pg.vmin, vmax = pg.vmax;
+
+    // page table of the tile: lane i holds block j0 + i (npg <= 8 < 64)
+    const int pid_l = (lane < npg && pg.bt_row) ? pg.bt_row[(int64_t)(j0 + lane) * pg.bt_sj] : -1;
+    const bool vis_l = lane < npg && (j0 + lane) * kBlock < vmax;
+    const bool ok_l = pid_l >= 0 && pid_l < pg.P;
+    uint64_t todo = __ballot(vis_l && ok_l);               // live pages, in block order
+    auto next_live = [&]() {
+        if (!todo) return -1;
+        const int pi = __builtin_ctzll(todo);
+        todo &= todo - 1;
+        return pi;
+    };
+    // this thread's slice of a page (threads below NLD): key tid / TPK, bytes
+    // 16*VPT*(tid % TPK) ..
+    const int skey = tid / TPK, spart = tid % TPK;
+    uint4 pv[2][VPT];                                      // the slices of the next pair of pages
+    auto load_page = [&](int pi, uint4 (&v)[VPT]) {
+        if (NLD < NT && tid >= NLD) return;
+        const int pid = __builtin_amdgcn_readlane(pid_l, pi);
+        const uint8_t *src = pg.index_k + (int64_t)pid * pg.k_sp + (int64_t)skey * pg.k_sb + 16 * VPT * spart;
+#pragma unroll
+        for (int h = 0; h < VPT; ++h) v[h] = *(const uint4 *)(src + 16 * h);
+    };
+    auto store_page = [&](const uint4 (&pv)[VPT], uint8_t *dst) {   // decode the slice to bf16 into dst
+        if (NLD < NT && tid >= NLD) return;
+        uint8_t *row = dst + skey * RB;
+#pragma unroll
+        for (int h = 0; h < VPT; ++h) {
+            const int u0 = 2 * (VPT * spart + h);          // bf16 unit of the slice's first 8 codes
+            uint4 lo, hi;
+            lo.x = fp8x2_to_bf16x2<false>(pv[h].x); lo.y = fp8x2_to_bf16x2<true>(pv[h].x);
+            lo.z = fp8x2_to_bf16x2<false>(pv[h].y); lo.w = fp8x2_to_bf16x2<true>(pv[h].y);
+            hi.x = fp8x2_to_bf16x2<false>(pv[h].z); hi.y = fp8x2_to_bf16x2<true>(pv[h].z);
+            hi.z = fp8x2_to_bf16x2<false>(pv[h].w); hi.w = fp8x2_to_bf16x2<true>(pv[h].w);
+            *(uint4 *)(row + ((u0 ^ (skey & (UPR - 1))) << 4)) = lo;
+            *(uint4 *)(row + (((u0 + 1) ^ (skey & (UPR - 1))) << 4)) = hi;
+        }
+    };
+    // Pages go through LDS two at a time (one barrier per pair).  The first
+    // pair is requested before the query rows: the other order was measured
+    // to be far slower.
+    int c0 = next_live(), c1 = next_live();
+    if (c0 >= 0) load_page(c0, pv[0]);
+    if (c1 >= 0) load_page(c1, pv[1]);
+
+    // Query rows, read coalesced.  In the MFMA operand layout consecutive
+    // lanes hold different query rows, and a global load in that layout
+    // touches a separate cache line for every lane of a 4-lane quad, several
+    // times slower than quads reading 64 contiguous bytes.  So each wave reads
+    // its 16*QT rows with whole rows across consecutive lanes and transposes
+    // them through 16 rows' worth of LDS of its own (below).
+    constexpr int RPL = 64 / UPR;               // rows per coalesced load
+    constexpr int LPT = 16 / RPL;               // loads per 16-row tile
+    uint4 qraw[QT][LPT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt)
+#pragma unroll
+        for (int l = 0; l < LPT; ++l) {
+            const int col = 16 * QT * wave + 16 * qt + l * RPL + lane / UPR;
+            qraw[qt][l] = *(const uint4 *)(qrow(col) + 8 * (lane % UPR));
+        }
+
+    // blocks without a live page: -inf for columns that see none of their
+    // keys, NaN for columns that see keys of a block whose page id is out of
+    // range
+    const uint64_t live = __ballot(vis_l && ok_l);
+    for (int idx = tid; idx < PQ * npg; idx += NT) {
+        const int qq = idx / npg, pi = idx % npg;
+        if (!((live >> pi) & 1)) {
+            const int v = vis(qq);
+            const int pid = __shfl(pid_l, pi);
+            const bool bad = (j0 + pi) * kBlock < v && !(pid >= 0 && pid < pg.P);
+            lds.sbuf[qq][pi] = bad ? __builtin_nanf("") : -INFINITY;
+        }
+    }
+
+    // B operand of S^T = K Q^T: for tile qt and k-step ks the lane holds
+    // column 16*QT*wave + 16*qt + lane%16 at d = 32*ks + 8*(lane/16) .. +7.
+    // Each wave transposes through 16 rows of LDS of its own (inside the page
+    // buffers, before any page is stored there), 16-byte units XOR-swizzled
+    // by row so that neither side has bank conflicts.  LDS accesses of one
+    // wave complete in order, so the wave needs no barrier of its own.
+    uint8_t *const stage = &lds.kb[0][0] + wave * (16 * RB);
+    uint4 qf[QT][KS];
+    int vt[QT];
+#pragma unroll
+    for (int qt = 0; qt < QT; ++qt) {
+        vt[qt] = vis(16 * QT * wave + 16 * qt + li);
+#pragma unroll
+        for (int l = 0; l < LPT; ++l) {
+            const int row = l * RPL + lane / UPR, unit = lane % UPR;
+            *(uint4 *)(stage + row * RB + ((unit ^ (row & (UPR - 1))) << 4)) = qraw[qt][l];
+        }
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int unit = 4 * ks + grp;
+            qf[qt][ks] = *(const uint4 *)(stage + li * RB + ((unit ^ (li & (UPR - 1))) << 4));
+        }
+    }
+
+    // first pair to LDS (once every wave is done with its transpose area);
+    // the next pair's slices on their way
+    __syncthreads();
+    if (c0 >= 0) store_page(pv[0], lds.kb[0]);
+    if (c1 >= 0) store_page(pv[1], lds.kb[1]);
+    int n0 = next_live(), n1 = next_live();
+    if (n0 >= 0) load_page(n0, pv[0]);
+    if (n1 >= 0) load_page(n1, pv[1]);
+    __syncthreads();
+
+    const float scale = pg.scale;
+    auto compute_page = [&](const uint8_t *buf, int cur) {
+        const int kbase = (j0 + cur) * kBlock;
+        float best[QT];
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) best[qt] = -INFINITY;
+        if (kbase + kBlock <= vmin) {                      // every key visible to every column
+            // tile kt+1's operands are read before tile kt's MFMAs, and tile
+            // kt's max is taken after tile kt+1's MFMAs are issued, so that
+            // neither the LDS latency nor the MFMA latency sits in the way
+            f32x4 acc[2][QT];
+            uint4 af[2][KS];
+            prefill_frag<DI>(buf, 0, li, grp, af[0]);
+#pragma unroll
+            for (int kt = 0; kt <= 8; ++kt) {
+                if (kt + 1 < 8) prefill_frag<DI>(buf, kt + 1, li, grp, af[(kt + 1) & 1]);
+                if (kt < 8) prefill_mma<DI, QT>(af[kt & 1], qf, acc[kt & 1]);
+                if (kt >= 1) {
+                    const f32x4 *done = acc[(kt - 1) & 1];
+#pragma unroll
+                    for (int qt = 0; qt < QT; ++qt) {
+                        best[qt] = max3f(best[qt], done[qt][0], done[qt][1]);
+                        best[qt] = max3f(best[qt], done[qt][2], done[qt][3]);
+                    }
+                }
+            }
+        } else {                                           // visibility edge: mask key >= V(column)
+            int lim[QT];
+#pragma unroll
+            for (int qt = 0; qt < QT; ++qt) lim[qt] = vt[qt] - kbase - 4 * grp;
+            for (int kt = 0; kt < 8; ++kt) {
+                uint4 a[KS];
+                prefill_frag<DI>(buf, kt, li, grp, a);
+                f32x4 acc[QT];
+                prefill_mma<DI, QT>(a, qf, acc);
+#pragma unroll
+                for (int qt = 0; qt < QT; ++qt) {
+                    float m[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m[e] = (kt * 16 + e < lim[qt]) ? acc[qt][e] : -INFINITY;
+                    best[qt] = max3f(best[qt], m[0], m[1]);
+                    best[qt] = max3f(best[qt], m[2], m[3]);
+                }
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < QT; ++qt) {
+            const float v = max_across_groups<16>(best[qt]);
+            if (grp == 0) lds.sbuf[16 * QT * wave + 16 * qt + li][cur] = v * scale;
+        }
+    };
+    for (int i = 0; c0 >= 0; ++i) {
+        const int b = 2 * (i & 1);
+        compute_page(lds.kb[b], c0);
+        if (c1 >= 0) compute_page(lds.kb[b + 1], c1);
+        // the other pair of buffers held the previous pair, done by every
+        // wave before the last barrier
+        const int nb = 2 - b;
+        if (n0 >= 0) store_page(pv[0], lds.kb[nb]);
+        if (n1 >= 0) store_page(pv[1], lds.kb[nb + 1]);
+        const int a0 = next_live(), a1 = next_live();
+        if (a0 >= 0) load_page(a0, pv[0]);
+        if (a1 >= 0) load_page(a1, pv[1]);
+        __syncthreads();
+        c0 = n0; c1 = n1;
+        n0 = a0; n1 = a1;
+    }
+}
+
+}  // namespace msa

@@ -5,19 +5,23 @@
 // Cacheon "Kernel ABI", "Attention block slots": attention.msa_block_score
 // (decode score sheet) and attention.msa_prefill_block_score (prefill).
 //
-// Two kernels:
+// Kernels:
 //  * score_valu  -- decode rows (T < 16 query tokens per row).  One wave per
 //    (row, group of <= 4 tokens, block).  The wave streams the 128-token page
 //    with coalesced 16-byte loads (8 lanes per 128-byte index row for FP8
 //    Di=128), decodes FP8 in registers to bf16 and accumulates with
 //    v_dot2_f32_bf16; the partial dots of a row are summed across its lanes
 //    with DPP, masked by visibility and max-reduced.
-//  * score_mfma  -- prefill rows (T >= 16).  A workgroup owns 128 query tokens
-//    of one row and a run of blocks; each page is staged once in LDS (FP8,
-//    XOR-swizzled) and every wave multiplies its 32 queries against it with
-//    v_mfma_f32_16x16x32_bf16 after exact FP8 -> bf16 decoding.
+//  * score_mfma_decode -- decode rows of up to 16 tokens with bf16 queries
+//    and an FP8 index: one page per wave on v_mfma_f32_16x16x32_bf16.
+//  * score_prefill -- prefill rows (T > 16).  A workgroup owns 256 or 512
+//    query tokens of one row and a run of at most 8 blocks; each page is
+//    decoded FP8 -> bf16 once into LDS and every wave multiplies its queries
+//    against it on MFMA (prefill_tile.h, shared with the ragged prefill
+//    score-to-selection call).
 #include "device_util.h"
 #include "msa_internal.h"
+#include "prefill_tile.h"
 #include "score_unit.h"
 
 namespace msa {
@@ -205,83 +209,23 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
 // ------------------------------------------------------------------ MFMA path
 //
 // Prefill rows (T > 16): a GEMM per row, S = Q_r K_r^T over the row's visible
-// keys, reduced to block maxima.  A workgroup of 8 waves (two per SIMD, one
-// workgroup per CU) owns 128*QT query tokens of a row (16*QT per wave = QT
-// MFMA column tiles of 16) and an even share of the blocks those tokens see
-// (at most kPMaxPC consecutive ones); the tiles are laid out so that the
-// workgroups of one query chunk run on one XCD.  The query rows are read
-// coalesced and transposed into the MFMA operand layout through LDS.
-//
-// Each live page is read once per workgroup with coalesced 16-byte loads
-// (every thread a 32-byte slice of a key row), decoded FP8 -> bf16 once and
-// stored to a bf16 page buffer in LDS, from which all 8 waves read their A
-// operands ready to use: the decode costs 16 VALU instructions per wave and
-// page instead of one per MFMA, and VALU issue does not overlap MFMA issue
-// well on a SIMD.  Pages go through LDS two at a time (four page buffers, one
-// barrier per pair); the next pair's slices are loaded into registers while
-// the current pair is multiplied, and decoded and stored after it.  Pages
-// that every token sees whole skip the causal mask.  The running block max
-// per (query, block) is staged in LDS and written out coalesced at the end.
+// keys, reduced to block maxima (prefill_tile.h).  A workgroup owns 128*QT
+// query tokens of a row (16*QT per wave = QT MFMA column tiles of 16) and an
+// even share of the blocks those tokens see (at most kPMaxPC consecutive
+// ones); the tiles are laid out so that the workgroups of one query chunk run
+// on one XCD.  The running block max per (query, block) is staged in LDS and
+// written out coalesced at the end.
 
-constexpr int kPWaves = 8;        // waves per workgroup, two per SIMD
-constexpr int kPMaxPC = 8;        // blocks per workgroup, at most
 constexpr int kPTargetWGs = 256;  // workgroups aimed for (one per CU)
-
-// max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
-// first, unlike fmaxf); the operands are dot products, never NaN (a NaN dot
-// product is outside the contract)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-}
-
-// bf16 A operands of the 16-key tile kt of the page in `buf`: key 16*kt +
-// lane%16; k-step ks covers d = 32*ks .. +31, lane group grp its d = 32*ks +
-// 8*grp .. +7: 16-byte unit 4*ks + grp of the key's bf16 row, stored
-// XOR-swizzled by the key.
-template <int DI>
-__device__ __forceinline__ void prefill_frag(const uint8_t *buf, int kt, int li, int grp, uint4 (&a)[DI / 32]) {
-    constexpr int KS = DI / 32, UPR = DI / 8;
-    const int key = kt * 16 + li;
-    const uint8_t *krow = buf + key * (DI * 2);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = *(const uint4 *)(krow + (((4 * ks + grp) ^ (key & (UPR - 1))) << 4));
-}
-
-// S^T tile of those keys against the wave's QT query tiles: acc[qt][e] =
-// q . k for key 16*kt + 4*grp + e and query column lane%16.
-template <int DI, int QT>
-__device__ __forceinline__ void prefill_mma(const uint4 (&a)[DI / 32], const uint4 (&qf)[QT][DI / 32],
-                                            f32x4 (&acc)[QT]) {
-    constexpr int KS = DI / 32;
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) acc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt)
-            acc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                __builtin_bit_cast(bf16x8, a[ks]), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
-}
 
 template <int DI, int QT>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_prefill_kernel(ScoreParams p, int WPC) {
-    constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
     constexpr int NT = 64 * kPWaves;            // threads per workgroup
-    constexpr int PQ = 16 * QT * kPWaves;       // query tokens per workgroup
-    constexpr int RB = DI * 2;                  // bytes per bf16 row (query or key)
-    constexpr int UPR = DI / 8;                 // 16-byte units per bf16 row
-    constexpr int VPT = kBlock * DI / (16 * NT) > 0 ? kBlock * DI / (16 * NT) : 1;  // 16-byte FP8 loads per slice
-    constexpr int TPK = DI / (16 * VPT);        // slices per key row
-    constexpr int NLD = TPK * kBlock;           // threads holding a slice (whole waves)
-    static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
-    __shared__ __attribute__((aligned(16))) uint8_t kb[4][kBlock * RB];   // two pairs of pages
-    __shared__ float sbuf[PQ][kPMaxPC + 1];
-    static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the first pair");
+    constexpr int PQ = PrefillLds<DI, QT>::PQ;  // query tokens per workgroup
+    __shared__ PrefillLds<DI, QT> lds;
 
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int grp = lane >> 4, li = lane & 15;
+    const int tid = threadIdx.x;
     const int QC = (p.T + PQ - 1) / PQ;
     // Query chunk c = r*QC + qc has WPC workgroups, tiles u = c*WPC + w.
     // Workgroups are dispatched round-robin over the 8 XCDs (XCD = blockIdx %
@@ -294,201 +238,38 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
     const int c = u / WPC, qc = c % QC, r = c / QC, w = u % WPC;
     const int L = clamp_len(p.seq_lens[(int64_t)r * p.sl_s], p.MB);
     const int tq0 = qc * PQ, tq1 = min(p.T, tq0 + PQ);
-    const int vmin = max(0, L - (p.T - 1 - tq0));        // keys seen by the WG's first token
-    const int vmax = max(0, L - (p.T - 1 - (tq1 - 1)));  // ... by its last
     const int64_t nrow = (int64_t)r * p.T;
+    PrefillPages pg;
+    pg.index_k = (const uint8_t *)p.index_k; pg.k_sp = p.k_sp; pg.k_sb = p.k_sb; pg.P = p.P;
+    pg.bt_row = p.bt + (int64_t)r * p.bt_sr; pg.bt_sj = p.bt_sj;
+    pg.vmin = max(0, L - (p.T - 1 - tq0));               // keys seen by the WG's first token
+    pg.vmax = max(0, L - (p.T - 1 - (tq1 - 1)));         // ... by its last
+    pg.scale = p.idx_scale;
     // Blocks the chunk's last token sees: 0 .. lp-1.  They are split evenly
     // over the chunk's workgroups (at most kPMaxPC each, by the choice of
     // WPC); blocks from lp on are seen by no token of the chunk: -inf, written
     // by workgroup w for every WPC-th of them.
-    const int lp = min(p.MB, (vmax + kBlock - 1) / kBlock);
-    const int j0 = (int)((int64_t)w * lp / WPC), npg = (int)((int64_t)(w + 1) * lp / WPC) - j0;
+    const int lp = min(p.MB, (pg.vmax + kBlock - 1) / kBlock);
+    pg.j0 = (int)((int64_t)w * lp / WPC);
+    pg.npg = (int)((int64_t)(w + 1) * lp / WPC) - pg.j0;
     for (int jd = lp + w; jd < p.MB; jd += WPC)
         for (int qq = tid; qq < tq1 - tq0; qq += NT)
             p.scores[(nrow + tq0 + qq) * p.sc_sn + (int64_t)jd * p.sc_sj] = -INFINITY;
 
-    // page table of the share: lane i holds block j0 + i (npg <= 8 < 64)
-    const int pid_l = lane < npg ? p.bt[(int64_t)r * p.bt_sr + (int64_t)(j0 + lane) * p.bt_sj] : -1;
-    const bool vis_l = lane < npg && (j0 + lane) * kBlock < vmax;
-    const bool ok_l = pid_l >= 0 && pid_l < p.P;
-    uint64_t todo = __ballot(vis_l && ok_l);               // live pages, in block order
-    auto next_live = [&]() {
-        if (!todo) return -1;
-        const int pi = __builtin_ctzll(todo);
-        todo &= todo - 1;
-        return pi;
+    // Columns past the row's last token read that token again; their scores
+    // are never stored, and no reduction mixes columns.
+    const uint16_t *q = (const uint16_t *)p.q_idx;
+    auto qrow = [&](int col) { return q + (nrow + min(p.T - 1, tq0 + col)) * p.q_sn; };
+    auto vis = [&](int col) {
+        const int t = tq0 + col;
+        return t < p.T ? max(0, L - (p.T - 1 - t)) : 0;
     };
-    // this thread's slice of a page (threads below NLD): key tid / TPK, bytes
-    // 16*VPT*(tid % TPK) ..
-    const int skey = tid / TPK, spart = tid % TPK;
-    uint4 pv[2][VPT];                                      // the slices of the next pair of pages
-    auto load_page = [&](int pi, uint4 (&v)[VPT]) {
-        if (NLD < NT && tid >= NLD) return;
-        const int pid = __builtin_amdgcn_readlane(pid_l, pi);
-        const uint8_t *src = (const uint8_t *)p.index_k + (int64_t)pid * p.k_sp + (int64_t)skey * p.k_sb +
-                             16 * VPT * spart;
-#pragma unroll
-        for (int h = 0; h < VPT; ++h) v[h] = *(const uint4 *)(src + 16 * h);
-    };
-    auto store_page = [&](const uint4 (&pv)[VPT], uint8_t *dst) {   // decode the slice to bf16 into dst
-        if (NLD < NT && tid >= NLD) return;
-        uint8_t *row = dst + skey * RB;
-#pragma unroll
-        for (int h = 0; h < VPT; ++h) {
-            const int u0 = 2 * (VPT * spart + h);          // bf16 unit of the slice's first 8 codes
-            uint4 lo, hi;
-            lo.x = fp8x2_to_bf16x2<false>(pv[h].x); lo.y = fp8x2_to_bf16x2<true>(pv[h].x);
-            lo.z = fp8x2_to_bf16x2<false>(pv[h].y); lo.w = fp8x2_to_bf16x2<true>(pv[h].y);
-            hi.x = fp8x2_to_bf16x2<false>(pv[h].z); hi.y = fp8x2_to_bf16x2<true>(pv[h].z);
-            hi.z = fp8x2_to_bf16x2<false>(pv[h].w); hi.w = fp8x2_to_bf16x2<true>(pv[h].w);
-            *(uint4 *)(row + ((u0 ^ (skey & (UPR - 1))) << 4)) = lo;
-            *(uint4 *)(row + (((u0 + 1) ^ (skey & (UPR - 1))) << 4)) = hi;
-        }
-    };
-    // Pages go through LDS two at a time (one barrier per pair).  The first
-    // pair is requested before the query rows: the other order was measured
-    // to be far slower.
-    int c0 = next_live(), c1 = next_live();
-    if (c0 >= 0) load_page(c0, pv[0]);
-    if (c1 >= 0) load_page(c1, pv[1]);
+    prefill_tile<DI, QT>(pg, qrow, vis, lds);
 
-    // Query rows, read coalesced.  In the MFMA operand layout consecutive
-    // lanes hold different query rows, and a global load in that layout
-    // touches a separate cache line for every lane of a 4-lane quad, several
-    // times slower than quads reading 64 contiguous bytes.  So each wave reads
-    // its 16*QT rows with whole rows across consecutive lanes and transposes
-    // them through 16 rows' worth of LDS of its own (below).  Columns past
-    // the row's last token read that token again; their scores are never
-    // stored, and no reduction mixes columns.
-    constexpr int RPL = 64 / UPR;               // rows per coalesced load
-    constexpr int LPT = 16 / RPL;               // loads per 16-row tile
-    uint4 qraw[QT][LPT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt)
-#pragma unroll
-        for (int l = 0; l < LPT; ++l) {
-            const int t = min(p.T - 1, tq0 + 16 * QT * wave + 16 * qt + l * RPL + lane / UPR);
-            qraw[qt][l] = *(const uint4 *)((const uint16_t *)p.q_idx + (nrow + t) * p.q_sn + 8 * (lane % UPR));
-        }
-
-    // blocks without a live page: -inf for tokens that see none of their keys,
-    // NaN for tokens that see keys of a block whose page id is out of range
-    const uint64_t live = __ballot(vis_l && ok_l);
-    for (int idx = tid; idx < PQ * npg; idx += NT) {
-        const int qq = idx / npg, pi = idx % npg;
-        if (!((live >> pi) & 1)) {
-            const int v = max(0, L - (p.T - 1 - (tq0 + qq)));
-            const int pid = __shfl(pid_l, pi);
-            const bool bad = (j0 + pi) * kBlock < v && !(pid >= 0 && pid < p.P);
-            sbuf[qq][pi] = bad ? __builtin_nanf("") : -INFINITY;
-        }
-    }
-
-    // B operand of S^T = K Q^T: for tile qt and k-step ks the lane holds query
-    // tq0 + 16*QT*wave + 16*qt + lane%16 at d = 32*ks + 8*(lane/16) .. +7.
-    // Each wave transposes through 16 rows of LDS of its own (inside the page
-    // buffers, before any page is stored there), 16-byte units XOR-swizzled
-    // by row so that neither side has bank conflicts.  LDS accesses of one
-    // wave complete in order, so the wave needs no barrier of its own.
-    uint8_t *const stage = &kb[0][0] + wave * (16 * RB);
-    uint4 qf[QT][KS];
-    int vt[QT];
-#pragma unroll
-    for (int qt = 0; qt < QT; ++qt) {
-        const int t = tq0 + 16 * QT * wave + 16 * qt + li;
-        vt[qt] = (t < p.T) ? max(0, L - (p.T - 1 - t)) : 0;
-#pragma unroll
-        for (int l = 0; l < LPT; ++l) {
-            const int row = l * RPL + lane / UPR, unit = lane % UPR;
-            *(uint4 *)(stage + row * RB + ((unit ^ (row & (UPR - 1))) << 4)) = qraw[qt][l];
-        }
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int unit = 4 * ks + grp;
-            qf[qt][ks] = *(const uint4 *)(stage + li * RB + ((unit ^ (li & (UPR - 1))) << 4));
-        }
-    }
-
-    // first pair to LDS (once every wave is done with its transpose area);
-    // the next pair's slices on their way
-    __syncthreads();
-    if (c0 >= 0) store_page(pv[0], kb[0]);
-    if (c1 >= 0) store_page(pv[1], kb[1]);
-    int n0 = next_live(), n1 = next_live();
-    if (n0 >= 0) load_page(n0, pv[0]);
-    if (n1 >= 0) load_page(n1, pv[1]);
-    __syncthreads();
-
-    const float scale = p.idx_scale;
-    auto compute_page = [&](const uint8_t *buf, int cur) {
-        const int kbase = (j0 + cur) * kBlock;
-        float best[QT];
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) best[qt] = -INFINITY;
-        if (kbase + kBlock <= vmin) {                      // every key visible to every token
-            // tile kt+1's operands are read before tile kt's MFMAs, and tile
-            // kt's max is taken after tile kt+1's MFMAs are issued, so that
-            // neither the LDS latency nor the MFMA latency sits in the way
-            f32x4 acc[2][QT];
-            uint4 af[2][KS];
-            prefill_frag<DI>(buf, 0, li, grp, af[0]);
-#pragma unroll
-            for (int kt = 0; kt <= 8; ++kt) {
-                if (kt + 1 < 8) prefill_frag<DI>(buf, kt + 1, li, grp, af[(kt + 1) & 1]);
-                if (kt < 8) prefill_mma<DI, QT>(af[kt & 1], qf, acc[kt & 1]);
-                if (kt >= 1) {
-                    const f32x4 *done = acc[(kt - 1) & 1];
-#pragma unroll
-                    for (int qt = 0; qt < QT; ++qt) {
-                        best[qt] = max3f(best[qt], done[qt][0], done[qt][1]);
-                        best[qt] = max3f(best[qt], done[qt][2], done[qt][3]);
-                    }
-                }
-            }
-        } else {                                           // causal edge: mask key >= V(token)
-            int lim[QT];
-#pragma unroll
-            for (int qt = 0; qt < QT; ++qt) lim[qt] = vt[qt] - kbase - 4 * grp;
-            for (int kt = 0; kt < 8; ++kt) {
-                uint4 a[KS];
-                prefill_frag<DI>(buf, kt, li, grp, a);
-                f32x4 acc[QT];
-                prefill_mma<DI, QT>(a, qf, acc);
-#pragma unroll
-                for (int qt = 0; qt < QT; ++qt) {
-                    float m[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) m[e] = (kt * 16 + e < lim[qt]) ? acc[qt][e] : -INFINITY;
-                    best[qt] = max3f(best[qt], m[0], m[1]);
-                    best[qt] = max3f(best[qt], m[2], m[3]);
-                }
-            }
-        }
-#pragma unroll
-        for (int qt = 0; qt < QT; ++qt) {
-            const float v = max_across_groups<16>(best[qt]);
-            if (grp == 0) sbuf[16 * QT * wave + 16 * qt + li][cur] = v * scale;
-        }
-    };
-    for (int i = 0; c0 >= 0; ++i) {
-        const int b = 2 * (i & 1);
-        compute_page(kb[b], c0);
-        if (c1 >= 0) compute_page(kb[b + 1], c1);
-        // the other pair of buffers held the previous pair, done by every
-        // wave before the last barrier
-        const int nb = 2 - b;
-        if (n0 >= 0) store_page(pv[0], kb[nb]);
-        if (n1 >= 0) store_page(pv[1], kb[nb + 1]);
-        const int a0 = next_live(), a1 = next_live();
-        if (a0 >= 0) load_page(a0, pv[0]);
-        if (a1 >= 0) load_page(a1, pv[1]);
-        __syncthreads();
-        c0 = n0; c1 = n1;
-        n0 = a0; n1 = a1;
-    }
+    const int npg = pg.npg, j0 = pg.j0;
     for (int idx = tid; idx < (tq1 - tq0) * npg; idx += NT) {
         const int qq = idx / npg, pi = idx % npg;
-        p.scores[(nrow + tq0 + qq) * p.sc_sn + (int64_t)(j0 + pi) * p.sc_sj] = sbuf[qq][pi];
+        p.scores[(nrow + tq0 + qq) * p.sc_sn + (int64_t)(j0 + pi) * p.sc_sj] = lds.sbuf[qq][pi];
     }
 }
 

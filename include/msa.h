@@ -162,10 +162,10 @@ size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
  *               again, so the same workspace can be reused (and replayed in a
  *               graph) without clearing.  Calls that share one workspace must
  *               not run concurrently.
- * D must be 64 or 128.  When Hq/Hkv == 16 with bf16 queries and FP8 caches the
- * QK^T and PV products run on bf16 MFMA tiles (FP8 decoded exactly, P rounded
- * to bf16); otherwise (bf16 or f32 caches, other head ratios) on vector ALUs
- * in fp32.
+ * D must be 64 or 128.  When Hq/Hkv == 16 with bf16 queries and FP8 or bf16
+ * caches the QK^T and PV products run on bf16 MFMA tiles (FP8 decoded exactly,
+ * P rounded to bf16); otherwise (f32 queries or caches, other head ratios) on
+ * vector ALUs in fp32.
  */
 void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
                        const msa_tensor *v_cache, const msa_tensor *block_table,
@@ -222,6 +222,69 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
                      float idx_scale, float sm_scale, float k_scale, float v_scale,
                      msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes msa_prefill_block_score needs: its plan (chunk and unit
+ * tables, the owner of every query-block row) and the query-block score sheet
+ * [num_q_heads, all_seqblock_q, parts, max_blocks] f32, parts = 1 unless
+ * block_size_q > 512.  Depends on these sizes only; 0 for sizes out of range.
+ */
+size_t msa_prefill_block_score_workspace_bytes(int32_t batch, int32_t num_q_heads,
+                                               int32_t all_seqblock_q, int32_t max_blocks,
+                                               int32_t block_size_q);
+
+/*
+ * Ragged prefill score-to-selection in one call.  Cacheon "Kernel ABI",
+ * "Attention block slots", attention.msa_prefill_block_score (the V2 call:
+ * score production and selection for the whole ragged batch, out_topk written
+ * once, unused cells -1; indices are logical block ids within the request).
+ *
+ * Request b owns the query tokens [cu_seqlens[b], cu_seqlens[b+1]) of q (its
+ * new tokens, in order) and the query-block rows [cu_seqblocks_q[b],
+ * cu_seqblocks_q[b+1]) of out_topk, one per block_size_q new tokens
+ * (ceil(new tokens / block_size_q) rows).  Its logical key sequence has
+ * seq_lens[b] keys; logical block j lives in page block_table[slot_ids[b]][j].
+ * For query head h and query block qb of request b (readings where the pages
+ * leave it open):
+ *   V      = min(seq_lens[b], prefix_lens[b] + qb * block_size_q)  keys visible
+ *   ncand  = ceil(V / 128)     candidate blocks 0 .. ncand-1
+ *   score_j = scale * max over the block's new tokens t and the keys s < V of
+ *             block j of sum_d q[t][h][d] * index_k[page(j)][s - 128 j][d]
+ *   forced = blocks j < init_blocks or j >= ncand - local_blocks
+ *   out_topk[h][cu_seqblocks_q[b] + qb] = the forced blocks (lower ids first,
+ *             at most topk), then the other candidates by score (ties to the
+ *             lower id), up to topk in all; ascending ids, padded with -1.
+ * Rows of out_topk that no request owns are all -1.  FP8 codes are decoded
+ * exactly, products run on bf16 MFMA tiles with fp32 sums.
+ *
+ *   q              [total_q, Hq, Di]  bf16   innermost stride 1, 16-byte aligned rows
+ *   index_k        [P, 128, Di]       fp8e4m3fn  one index head; rows 16-byte aligned
+ *   block_table    [slots, MB] i32    any strides, 1 <= MB <= 2048
+ *   slot_ids, seq_lens, prefix_lens   [batch] i32 (seq_lens[b] <= MB*128)
+ *   cu_seqlens, cu_seqblocks_q        [batch+1] i32, non-decreasing from 0
+ *   block_size_q >= 1; block_size_k must be 128; topk >= 1;
+ *   init_blocks, local_blocks >= 0; scale > 0, finite
+ *   out_topk       [Hq, all_seqblock_q, topk] i32 OUT  any strides;
+ *                  all_seqblock_q >= cu_seqblocks_q[batch]
+ *   workspace      at least msa_prefill_block_score_workspace_bytes(batch, Hq,
+ *                  all_seqblock_q, MB, block_size_q) bytes, 256-byte aligned,
+ *                  owned by the caller; needs no initialisation (each call
+ *                  writes what it reads).  Calls sharing a workspace must not
+ *                  run concurrently.
+ * Di must be 64 or 128; batch at most 8192.  The page-size and length hints
+ * of the pages' signature (max_seqlen_q/k, max_seqblock_q) are not needed:
+ * the call plans its work on the device.  Inputs outside this contract
+ * (inconsistent offsets, page ids outside [0, P), NaN dot products) never
+ * cause an access outside the given tensors, but their rows are unspecified.
+ */
+void msa_prefill_block_score(const msa_tensor *q, const msa_tensor *index_k,
+                             const msa_tensor *block_table, const msa_tensor *slot_ids,
+                             const msa_tensor *cu_seqlens, const msa_tensor *seq_lens,
+                             const msa_tensor *prefix_lens, int32_t block_size_q,
+                             int32_t block_size_k, int32_t topk, int32_t init_blocks,
+                             int32_t local_blocks, float scale, const msa_tensor *cu_seqblocks_q,
+                             msa_tensor *out_topk, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Error code recorded by the most recent failing call on this thread, then
  * reset to MSA_OK.  Returns MSA_OK when no call failed since the last read. */

@@ -66,7 +66,7 @@ def _load():
             lib.orc_prefill_select.restype = ctypes.c_int
             lib.orc_prefill_select.argtypes = [vp, ctypes.c_int, i64, i64, i64, vp, ctypes.c_int, i64,
                                                i64, vp, i64, i64, vp, vp, vp, vp, i64, i64, i64, i64,
-                                               i64, dbl, vp, i64, i64, i64, vp, vp]
+                                               i64, dbl, vp, i64, i64, i64, vp, vp, vp]
             lib.orc_dense_attention.restype = ctypes.c_int
             lib.orc_dense_attention.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp,
                                                 i64, i64, i64, i64, i64, i64, i64, i64,
@@ -200,11 +200,14 @@ def sparse_decode(q, k_cache, v_cache, block_table, seq_lens, topk_idx, T: int,
 
 def prefill_select(q, index_k, block_table, slot_ids, cu_seqlens, seq_lens, prefix_lens,
                    block_size_q: int, topk: int, init_blocks: int, local_blocks: int, scale: float,
-                   cu_seqblocks_q, all_qb: int, threads: int = 1, return_scores: bool = False):
+                   cu_seqblocks_q, all_qb: int, threads: int = 1, return_scores: bool = False,
+                   rows=None):
     """Prefill score-to-selection over a ragged batch (attention.msa_prefill_block_score):
     out_topk [Hq, all_qb, topk] int32, and with ``return_scores`` also the
     scores [Hq, all_qb, MB] float64 (-inf where a block is no candidate).
-    q [total_q, Hq, Di]; index_k [P, B, Di]; block_table [slots, MB]."""
+    q [total_q, Hq, Di]; index_k [P, B, Di]; block_table [slots, MB].  ``rows``
+    (bool [Hq, all_qb]) restricts the work to the marked rows; the others stay
+    -1 (and -inf)."""
     lib = _load()
     qa, qd = _raw(q)
     ka, kd = _raw(index_k)
@@ -217,13 +220,17 @@ def prefill_select(q, index_k, block_table, slot_ids, cu_seqlens, seq_lens, pref
     batch = arrs[0].shape[0]
     out = np.full((Hq, all_qb, topk), -1, dtype=np.int32)
     sc = np.full((Hq, all_qb, MB), -np.inf) if return_scores else None
+    mask = None
+    if rows is not None:
+        mask = np.ascontiguousarray(np.asarray(rows, dtype=bool).reshape(Hq, all_qb), dtype=np.uint8)
 
     def run(h0, h1):
         return lib.orc_prefill_select(_ptr(qa), qd, total_q, Hq, Di, _ptr(ka), kd, P, B, _ptr(bt),
                                       nslots, MB, _ptr(arrs[0]), _ptr(arrs[1]), _ptr(arrs[2]),
                                       _ptr(arrs[3]), batch, block_size_q, topk, init_blocks,
                                       local_blocks, float(scale), _ptr(arrs[4]), all_qb, h0, h1,
-                                      _ptr(out), _ptr(sc) if sc is not None else None)
+                                      _ptr(mask) if mask is not None else None, _ptr(out),
+                                      _ptr(sc) if sc is not None else None)
 
     with ThreadPoolExecutor(max_workers=max(1, min(threads, Hq))) as ex:
         for rc in ex.map(lambda ab: run(*ab), _ranges(0, Hq, threads)):

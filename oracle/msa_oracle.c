@@ -214,6 +214,8 @@ int orc_select_topk(const double *scores, int64_t N, int64_t MB, int64_t k, int3
  *  - out_topk [Hq, all_qb, topk] row cu_seqblocks_q[b] + qb; rows no query
  *    block owns hold -1.
  * scores, when not NULL, receives [Hq, all_qb, MB] (-inf where no candidate).
+ * rows, when not NULL, is a [Hq, all_qb] mask: only the rows it marks are
+ * computed (the others stay -1 / -inf), so that large batches can be sampled.
  */
 int orc_prefill_select(const void *q, int q_dtype, int64_t total_q, int64_t Hq, int64_t Di,
                        const void *index_k, int k_dtype, int64_t P, int64_t B,
@@ -222,7 +224,7 @@ int orc_prefill_select(const void *q, int q_dtype, int64_t total_q, int64_t Hq, 
                        const int32_t *prefix_lens, int64_t batch, int64_t bsq, int64_t topk,
                        int64_t init_blocks, int64_t local_blocks, double scale,
                        const int32_t *cu_seqblocks_q, int64_t all_qb, int64_t h_begin, int64_t h_end,
-                       int32_t *out_topk, double *scores)
+                       const uint8_t *rows, int32_t *out_topk, double *scores)
 {
     if (Hq < 1 || Di < 1 || B < 1 || MB < 1 || bsq < 1 || topk < 1 || init_blocks < 0 ||
         local_blocks < 0 || !(scale > 0) || h_begin < 0 || h_end > Hq || batch < 0)
@@ -252,6 +254,8 @@ int orc_prefill_select(const void *q, int q_dtype, int64_t total_q, int64_t Hq, 
         }
         for (int64_t h = h_begin; h < h_end && rc == ORC_OK; h++) {
             for (int64_t qb = 0; qb < nqb && rc == ORC_OK; qb++) {
+                if (rows && !rows[h * all_qb + row0 + qb])
+                    continue;                     /* row not asked for: stays -1 / -inf */
                 int64_t V = (int64_t)prefix_lens[b] + qb * bsq;
                 if (V > seq_lens[b])
                     V = seq_lens[b];

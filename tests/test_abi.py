@@ -179,3 +179,52 @@ def test_decode_step_rejects(msa):
     _expect(msa, 5, f, *with_(9, 64))                                     # block size
     assert torch.isnan(c["scores"]).all() and (c["topk"] == -7).all()
     assert torch.isnan(c["out"].float()).all()
+
+
+def test_prefill_workspace_bytes(msa):
+    f = msa.msa_prefill_block_score_workspace_bytes
+    a = f(4, 4, 80, 104, 64)
+    assert a == f(4, 4, 80, 104, 64) and a > 0 and a % 256 == 0
+    assert a >= 4 * 80 * 104 * 4                      # the query-block score sheet
+    # query blocks longer than a chunk keep one sheet per 512-token part
+    assert f(1, 2, 3, 10, 2048) >= 2 * 3 * 4 * 10 * 4
+    assert f(4, 0, 80, 104, 64) == 0 and f(4, 4, 80, 0, 64) == 0 and f(4, 4, 80, 104, 0) == 0
+
+
+def test_prefill_block_score_rejects(msa):
+    batch, total_q, Hq, Di, P, MB, all_qb, k = 2, 100, 4, 128, 20, 8, 3, 4
+    i32 = lambda *s: torch.zeros(*s, dtype=torch.int32)
+    out = torch.full((Hq, all_qb, k), -7, dtype=torch.int32)
+    ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    base = [torch.zeros(total_q, Hq, Di, dtype=torch.bfloat16),
+            torch.zeros(P, 128, Di, dtype=torch.uint8), i32(3, MB), i32(batch), i32(batch + 1),
+            i32(batch), i32(batch), 64, 128, k, 1, 2, 0.05, i32(batch + 1), out, ws]
+    f = msa.msa_prefill_block_score
+
+    def with_(i, v):
+        a = list(base)
+        a[i] = v
+        return a
+
+    _expect(msa, 2, f, *with_(0, base[0].float()))                        # q must be bf16
+    _expect(msa, 2, f, *with_(1, base[1].float()))                        # index must be FP8
+    _expect(msa, 2, f, *with_(3, torch.zeros(batch, dtype=torch.int64)))  # int32 offsets
+    _expect(msa, 3, f, *with_(4, i32(batch)))                             # cu_seqlens [batch+1]
+    _expect(msa, 3, f, *with_(13, i32(batch + 2)))                        # cu_seqblocks_q
+    _expect(msa, 3, f, *with_(9, k + 1))                                  # topk vs out width
+    _expect(msa, 3, f, *with_(14, torch.zeros(Hq + 1, all_qb, k, dtype=torch.int32)))
+    a = with_(0, torch.zeros(total_q, Hq, 32, dtype=torch.bfloat16))     # Di = 32
+    a[1] = torch.zeros(P, 128, 32, dtype=torch.uint8)
+    _expect(msa, 5, f, *a)
+    _expect(msa, 5, f, *with_(8, 64))                                     # block_size_k
+    _expect(msa, 5, f, *with_(2, i32(3, 4096)))                           # MB > 2048
+    _expect(msa, 7, f, *with_(7, 0))                                      # block_size_q
+    _expect(msa, 7, f, *with_(10, -1))                                    # init_blocks
+    _expect(msa, 7, f, *with_(11, -1))                                    # local_blocks
+    _expect(msa, 7, f, *with_(12, 0.0))                                   # scale
+    _expect(msa, 7, f, *with_(12, float("nan")))
+    _expect(msa, 4, f, *with_(0, torch.zeros(total_q, Hq, 2 * Di, dtype=torch.bfloat16)[..., ::2]))
+    _expect(msa, 6, f, *with_(15, None))                                  # no workspace
+    _expect(msa, 6, f, *with_(15, ws[:256]))                              # too small
+    _expect(msa, 6, f, *with_(15, ws[1:]))                                # misaligned
+    assert (out == -7).all()

@@ -532,3 +532,17 @@ def test_prefill_select_forced_blocks(orc):
             V = min(int(pb.seq_lens[b]), int(pb.prefix_lens[b]) + qb * pb.block_size_q)
             row = got[0, int(pb.cu_seqblocks_q[b]) + qb]
             assert list(row[row >= 0]) == list(range(-(-V // pb.B)))
+
+
+def test_prefill_select_row_mask_computes_only_marked_rows(orc):
+    """The row mask (used to sample large batches) changes no computed row:
+    marked rows equal the unmasked call's, unmarked rows stay -1 / -inf."""
+    pb = _tiny_batches()[0]
+    args = (pb.q, pb.index_k, pb.block_table, pb.slot_ids, pb.cu_seqlens, pb.seq_lens,
+            pb.prefix_lens, pb.block_size_q, pb.topk, pb.init_blocks, pb.local_blocks, pb.scale,
+            pb.cu_seqblocks_q, pb.all_qb)
+    full, fsc = orc.prefill_select(*args, return_scores=True)
+    mask = np.random.default_rng(16).random((pb.Hq, pb.all_qb)) < 0.5
+    got, sc = orc.prefill_select(*args, return_scores=True, rows=mask, threads=2)
+    assert np.array_equal(got[mask], full[mask]) and np.array_equal(sc[mask], fsc[mask])
+    assert (got[~mask] == -1).all() and np.isneginf(sc[~mask]).all()
