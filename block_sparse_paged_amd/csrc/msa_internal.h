@@ -63,8 +63,8 @@ struct ReduceParams {
 // into chunks of one request: up to kPrefillCols (token, query head) columns
 // covering whole query blocks of all heads (bsq*Hq <= kPrefillCols), whole
 // query blocks of a group of heads (bsq <= kPrefillCols), or a part of one
-// query block of one head; a chunk's blocks are cut into units of at most
-// kPMaxPC consecutive blocks, one unit per workgroup pass.
+// query block of one head; the scoring workgroups share the chunks' visible
+// blocks ("pages") evenly, in tiles of at most kPMaxPC blocks of one chunk.
 constexpr int kPrefillCols = 512;            // columns of a chunk (one 8-wave tile of 4 MFMA column tiles)
 constexpr int kPlanMaxBatch = 8192;          // requests one call takes
 
@@ -74,7 +74,7 @@ struct PrefillGeom {
     int32_t NP;     // parts per query block (1 unless bsq > kPrefillCols)
     int32_t HG;     // head groups: ceil(Hq / hc)
     int64_t Cmax;   // chunks at most
-    int64_t Umax;   // units at most
+    int64_t Pmax;   // pages (chunk x visible block) at most
 };
 
 struct PrefillSelParams {
@@ -87,12 +87,9 @@ struct PrefillSelParams {
     int32_t total_q, Hq, P, nslots, MB, batch, bsq, topk, init_blocks, local_blocks, all_qb;
     float scale;
     PrefillGeom g;
-    int32_t nwg;                                       // workgroups of the scoring launch
+    int32_t nwg;                                       // workgroups of the scoring launch (multiple of 8)
     // workspace (msa_prefill_block_score_workspace_bytes)
-    int32_t *hdr;       // [0] units, [1] blocks per unit, [2] chunks
     int32_t *rowinfo;   // [all_qb]: request owning the query-block row, or -1
-    int4 *chunks;       // [Cmax][3] chunk descriptors
-    int4 *units;        // [Umax]: chunk, first block, blocks
     float *ws;          // [Hq, all_qb, NP, MB] query-block maxima
 };
 

@@ -9,18 +9,23 @@
 // to the lower id; ids are written ascending into out_topk[h][row(b, qb)] and
 // padded with -1, and rows no request owns are all -1.
 //
-// Three launches on the caller's stream, no host synchronisation:
-//  1. plan (one workgroup): cuts the batch into chunks of (token, head)
-//     columns of one request (kPrefillCols at most) and each chunk's visible
-//     blocks into units of G consecutive blocks, with G chosen from the live
-//     totals so that the units fill the CUs evenly; writes the chunk and unit
-//     tables and the owner of every query-block row to the workspace.
-//  2. scoring (one persistent workgroup per CU): each unit is one
-//     prefill_tile (MFMA over LDS-staged bf16 pages) followed by the max over
-//     each query block's tokens, written to the [Hq, all_qb, NP, MB] sheet in
-//     the workspace.  Consecutive units (same chunk, then neighbouring chunks
-//     of one request) run on one XCD so that they share its L2.
-//  3. selection (one wave per (head, query-block row)): forced blocks become
+// Two launches on the caller's stream, no host synchronisation:
+//  1. scoring (one persistent workgroup per CU).  The work is cut into chunks
+//     of (token, head) columns of one request (kPrefillCols at most, whole
+//     query blocks where they fit), and each chunk into its visible blocks
+//     ("pages"), in the order request, query-block group, head group, part.
+//     Every workgroup first derives the page count of every request from the
+//     offsets alone (a prologue over the batch, in LDS), then takes the
+//     contiguous page range [r*T/nwg, (r+1)*T/nwg) of the T pages: the shares
+//     differ by at most one page whatever the mix of lengths.  It walks its
+//     range in tiles of at most kPMaxPC pages of one chunk (prefill_tile: MFMA
+//     over LDS-staged bf16 pages) and reduces each tile to the max over each
+//     query block's tokens, written to the [Hq, all_qb, NP, MB] sheet in the
+//     workspace.  XCD x holds the ranges of 1/8 of the pages, so neighbouring
+//     chunks of one request (same pages) and the tiles of one chunk (same
+//     queries) share its L2.  The prologue also records which request owns
+//     each query-block row.
+//  2. selection (one wave per (head, query-block row)): forced blocks become
 //     the largest keys, the others their order-preserving score keys, and the
 //     wave-level radix select of select_unit.h takes the topk.
 #include "device_util.h"
@@ -32,8 +37,6 @@ namespace msa {
 
 namespace {
 
-constexpr int kPlanThreads = 1024;
-
 // keys visible to query block qb of a request: min(seq, prefix + qb*bsq),
 // never below 0 (seqc is already clamped to [0, MB*B])
 __device__ __forceinline__ int qb_visible(int seqc, int pre, int64_t qb, int64_t bsq) {
@@ -43,8 +46,9 @@ __device__ __forceinline__ int qb_visible(int seqc, int pre, int64_t qb, int64_t
 
 __device__ __forceinline__ int ld(const int32_t *a, int64_t s, int64_t i) { return a[i * s]; }
 
-// exclusive prefix sum over the kPlanThreads threads of the workgroup; total
-// gets the sum of all.  wsum: 16 ints of LDS.
+// exclusive prefix sum over the NT threads of the workgroup; total gets the
+// sum of all.  wsum: NT/64 ints of LDS.
+template <int NT>
 __device__ __forceinline__ int block_excl_scan(int x, int *wsum, int &total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int inc = wave_prefix_sum(x);
@@ -52,7 +56,7 @@ __device__ __forceinline__ int block_excl_scan(int x, int *wsum, int &total) {
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < kPlanThreads / 64; ++w) {
+    for (int w = 0; w < NT / 64; ++w) {
         const int v = wsum[w];
         base += w < wave ? v : 0;
         tot += v;
@@ -62,139 +66,164 @@ __device__ __forceinline__ int block_excl_scan(int x, int *wsum, int &total) {
     return base + inc - x;
 }
 
-__global__ __launch_bounds__(kPlanThreads) void prefill_plan_kernel(PrefillSelParams p) {
-    __shared__ int cs[kPlanMaxBatch + 1];              // first chunk of each request
-    __shared__ int wsum[kPlanThreads / 64];
-    __shared__ int gsum[8][kPlanThreads / 64];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const PrefillGeom g = p.g;
-    const int64_t bsq = p.bsq;
-    const int per_qc = g.HG * g.NP;                   // chunks per group of nqc query blocks
+// what the kernels read of request b
+struct Req {
+    int q0, nq, nqb, row0, seqc, pre, slot;
+    int nqcs;      // query-block groups: ceil(nqb / nqc)
+};
 
-    for (int r = tid; r < p.all_qb; r += kPlanThreads) p.rowinfo[r] = -1;
-
-    // chunks per request, prefix-summed into cs
-    int run = 0;
-    for (int base = 0; base < p.batch; base += kPlanThreads) {
-        const int b = base + tid;
-        int n = 0;
-        if (b < p.batch) {
-            const int nqb = min(max(ld(p.cu_qb, p.s_cq, b + 1) - ld(p.cu_qb, p.s_cq, b), 0), p.all_qb);
-            n = (nqb + g.nqc - 1) / g.nqc * per_qc;
-        }
-        int tot;
-        const int ex = block_excl_scan(n, wsum, tot);
-        if (b < p.batch) cs[b] = run + ex;
-        run += tot;
-    }
-    const int C = (int)min((int64_t)run, g.Cmax);
-    if (tid == 0) cs[p.batch] = run;
-    __syncthreads();                                   // cs complete, rowinfo cleared
-
-    // chunk descriptors; units per chunk for every G in 1..8
-    int ucount[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int c = tid; c < C; c += kPlanThreads) {
-        // the request: the last b with cs[b] <= c (it has cs[b+1] > c)
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (cs[mid] <= c) lo = mid; else hi = mid - 1;
-        }
-        const int b = lo, k = c - cs[b];
-        const int qc = k / per_qc, rem = k - qc * per_qc, hg = rem / g.NP, part = rem - hg * g.NP;
-        const int q0 = ld(p.cu_seqlens, p.s_cu, b);
-        const int nq = max(0, ld(p.cu_seqlens, p.s_cu, b + 1) - q0);
-        const int row0 = ld(p.cu_qb, p.s_cq, b);
-        const int nqb = min(max(ld(p.cu_qb, p.s_cq, b + 1) - row0, 0), p.all_qb);
-        const int seqc = min(max(ld(p.seq_lens, p.s_sl, b), 0), p.MB * kBlock);
-        const int pre = ld(p.prefix_lens, p.s_pl, b);
-        const int slot = ld(p.slot_ids, p.s_slot, b);
-        const int64_t qstart = (int64_t)qc * g.nqc * bsq;
-        const int64_t tok0 = qstart + (int64_t)part * kPrefillCols;
-        int64_t tok1 = qstart + min((int64_t)g.nqc * bsq, (int64_t)(part + 1) * kPrefillCols);
-        tok1 = min(tok1, min((int64_t)nq, (int64_t)nqb * bsq));
-        const int ntok = (int)max(tok1 - tok0, (int64_t)0);
-        const int lp = ntok > 0 ? (qb_visible(seqc, pre, (tok1 - 1) / bsq, bsq) + kBlock - 1) / kBlock : 0;
-        p.chunks[3 * (int64_t)c] = make_int4(slot, (int)min((int64_t)q0 + tok0, (int64_t)0x7fffffff), ntok,
-                                             hg * g.hc);
-        p.chunks[3 * (int64_t)c + 1] = make_int4((int)min(tok0, (int64_t)0x7fffffff), seqc, pre, row0);
-        p.chunks[3 * (int64_t)c + 2] = make_int4(part, lp, 0, 0);
-#pragma unroll
-        for (int G = 1; G <= 8; ++G) ucount[G - 1] += (lp + G - 1) / G;
-        if (hg == 0 && part == 0)
-            for (int qb = qc * g.nqc; qb < min(nqb, qc * g.nqc + g.nqc); ++qb)
-                if (row0 + qb >= 0 && row0 + qb < p.all_qb) p.rowinfo[row0 + qb] = b;
-    }
-
-    // G: fewest rounds of units over the workgroups, each round priced at G
-    // pages plus the fixed cost of a unit (its queries, its first pages'
-    // latency), about 1.5 pages
-#pragma unroll
-    for (int G = 0; G < 8; ++G) {
-        int v = ucount[G];
-        v += __shfl_xor(v, 1); v += __shfl_xor(v, 2); v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8); v += __shfl_xor(v, 16); v += __shfl_xor(v, 32);
-        if (lane == 0) gsum[G][wave] = v;
-    }
-    __syncthreads();
-    int G = 8;
-    int64_t best = -1;
-    for (int c = 1; c <= 8; ++c) {
-        int64_t L = 0;
-        for (int w = 0; w < kPlanThreads / 64; ++w) L += gsum[c - 1][w];
-        if (L > g.Umax) continue;
-        const int64_t cost = (L + p.nwg - 1) / p.nwg * (2 * c + 3);
-        if (best < 0 || cost <= best) { best = cost; G = c; }
-    }
-
-    // unit table: chunk c's units are consecutive, in block order
-    run = 0;
-    for (int base = 0; base < C; base += kPlanThreads) {
-        const int c = base + tid;
-        const int lp = c < C ? p.chunks[3 * (int64_t)c + 2].y : 0;   // written by this thread above
-        const int n = (lp + G - 1) / G;
-        int tot;
-        const int ex = block_excl_scan(n, wsum, tot);
-        for (int i = 0; i < n; ++i) {
-            const int64_t u = (int64_t)run + ex + i;
-            if (u < g.Umax) p.units[u] = make_int4(c, i * G, min(G, lp - i * G), 0);
-        }
-        run += tot;
-    }
-    if (tid == 0) {
-        p.hdr[0] = (int)min((int64_t)run, g.Umax);
-        p.hdr[1] = G;
-        p.hdr[2] = C;
-    }
+__device__ __forceinline__ Req load_req(const PrefillSelParams &p, int b) {
+    Req r;
+    r.q0 = ld(p.cu_seqlens, p.s_cu, b);
+    r.nq = max(0, ld(p.cu_seqlens, p.s_cu, b + 1) - r.q0);
+    r.row0 = ld(p.cu_qb, p.s_cq, b);
+    r.nqb = min(max(ld(p.cu_qb, p.s_cq, b + 1) - r.row0, 0), p.all_qb);
+    r.seqc = min(max(ld(p.seq_lens, p.s_sl, b), 0), p.MB * kBlock);
+    r.pre = ld(p.prefix_lens, p.s_pl, b);
+    r.slot = ld(p.slot_ids, p.s_slot, b);
+    r.nqcs = (r.nqb + p.g.nqc - 1) / p.g.nqc;
+    return r;
 }
+
+// tokens [tok0, tok1) of chunk (query-block group qc, part) of a request
+__device__ __forceinline__ void chunk_tokens(const PrefillSelParams &p, const Req &r, int qc, int part,
+                                             int64_t &tok0, int64_t &tok1) {
+    const int64_t bsq = p.bsq, qstart = (int64_t)qc * p.g.nqc * bsq;
+    tok0 = qstart + (int64_t)part * kPrefillCols;
+    tok1 = qstart + min((int64_t)p.g.nqc * bsq, (int64_t)(part + 1) * kPrefillCols);
+    tok1 = min(tok1, min((int64_t)r.nq, (int64_t)r.nqb * bsq));
+}
+
+// pages of a chunk: the blocks its last query block sees (0 for no tokens).
+// Division-free (it runs once per chunk in every workgroup's prologue): the
+// last query block of group qc is min(nqb, (qc+1)*nqc) - 1, and a part of a
+// query block (NP > 1, nqc = 1) belongs to query block qc.
+__device__ __forceinline__ int chunk_pages(const PrefillSelParams &p, const Req &r, int qc, int part) {
+    const int64_t bsq = p.bsq;
+    const int64_t tok0 = (int64_t)qc * p.g.nqc * bsq + (int64_t)part * kPrefillCols;
+    if (tok0 >= min((int64_t)r.nq, (int64_t)r.nqb * bsq)) return 0;
+    const int qbl = p.g.NP > 1 ? qc : min(r.nqb - 1, (qc + 1) * p.g.nqc - 1);
+    return (qb_visible(r.seqc, r.pre, qbl, bsq) + kBlock - 1) / kBlock;
+}
+
+// blocks per scoring tile: as many as LDS holds next to the four page
+// buffers, so that most workgroups' shares are one tile
+constexpr int kRaggedPC = 14;
+// requests whose fields the prologue keeps in LDS (larger batches re-read them)
+constexpr int kLdsReqs = 512;
 
 template <int DI>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_score_ragged_kernel(PrefillSelParams p) {
     constexpr int QT = kPrefillCols / (16 * kPWaves);
     constexpr int NT = 64 * kPWaves;
-    static_assert(PrefillLds<DI, QT>::PQ == kPrefillCols, "chunk columns = tile columns");
-    __shared__ PrefillLds<DI, QT> lds;
+    using Lds = PrefillLds<DI, QT, kRaggedPC>;
+    static_assert(Lds::PQ == kPrefillCols, "chunk columns = tile columns");
+    static_assert(sizeof(Lds::kb) >= 4 * (kPlanMaxBatch + 4 + 8 * kLdsReqs), "prologue tables in the page buffers");
+    __shared__ Lds lds;
+    __shared__ int wsum[NT / 64];
     const int tid = threadIdx.x, lane = tid & 63;
-    const int L = p.hdr[0];
-    // XCD x (= blockIdx % 8) takes the units [x*per, (x+1)*per) of every
-    // round of nwg units
-    const int per = p.nwg / 8;
-    const int first = (int)(blockIdx.x % 8) * per + (int)(blockIdx.x / 8);
-    const int hc = p.g.hc, NP = p.g.NP;
+    const PrefillGeom g = p.g;
     const int64_t bsq = p.bsq;
-    for (int u = first; u < L; u += p.nwg) {
-        const int4 un = p.units[u];
-        const int4 d0 = p.chunks[3 * (int64_t)un.x], d1 = p.chunks[3 * (int64_t)un.x + 1];
-        const int part = p.chunks[3 * (int64_t)un.x + 2].x;
-        const int slot = d0.x, qrow0 = max(d0.y, 0), ntok = d0.z, h0 = d0.w;
-        const int tok0 = d1.x, seqc = d1.y, pre = d1.z, row0 = d1.w;
-        const int qbf = (int)(tok0 / bsq), qbl = (int)((tok0 + ntok - 1) / bsq);
+    // XCD x (= blockIdx % 8) holds the ranges x*nwg/8 .. (x+1)*nwg/8 - 1
+    const int rng = (int)(blockIdx.x % 8) * (p.nwg / 8) + (int)(blockIdx.x / 8);
+    // the rows of request rng (written at the end, read now)
+    const int ri_row0 = rng < p.batch ? ld(p.cu_qb, p.s_cq, rng) : 0;
+    const int ri_end = rng < p.batch ? ld(p.cu_qb, p.s_cq, rng + 1) : 0;
+    const int rows_owned = ld(p.cu_qb, p.s_cq, p.batch);
+
+    // pages of every request, prefix-summed into PS, and the request fields
+    // for small batches, in the page buffers (before any page is staged)
+    int *PS = (int *)&lds.kb[0][0];
+    int *RQ = PS + ((kPlanMaxBatch + 4) & ~3);          // 16-byte aligned
+    const bool rq_lds = p.batch <= kLdsReqs;
+    int run = 0;
+    for (int base = 0; base < p.batch; base += NT) {
+        const int b = base + tid;
+        int n = 0;
+        if (b < p.batch) {
+            const Req r = load_req(p, b);
+            for (int qc = 0; qc < r.nqcs; ++qc)
+                for (int part = 0; part < g.NP; ++part) n += chunk_pages(p, r, qc, part);
+            n *= g.HG;
+            if (rq_lds) {
+                *(int4 *)(RQ + 8 * b) = make_int4(r.q0, r.nq, r.nqb, r.row0);
+                *(int4 *)(RQ + 8 * b + 4) = make_int4(r.seqc, r.pre, r.slot, r.nqcs);
+            }
+        }
+        int tot;
+        const int ex = block_excl_scan<NT>(n, wsum, tot);
+        if (b < p.batch) PS[b] = run + ex;
+        run += tot;
+    }
+    __syncthreads();                                   // PS and RQ complete
+    auto req_lds = [&](int b) {
+        if (!rq_lds) return load_req(p, b);
+        const int4 a = *(const int4 *)(RQ + 8 * b), c = *(const int4 *)(RQ + 8 * b + 4);
+        Req r;
+        r.q0 = __builtin_amdgcn_readfirstlane(a.x); r.nq = __builtin_amdgcn_readfirstlane(a.y);
+        r.nqb = __builtin_amdgcn_readfirstlane(a.z); r.row0 = __builtin_amdgcn_readfirstlane(a.w);
+        r.seqc = __builtin_amdgcn_readfirstlane(c.x); r.pre = __builtin_amdgcn_readfirstlane(c.y);
+        r.slot = __builtin_amdgcn_readfirstlane(c.z); r.nqcs = __builtin_amdgcn_readfirstlane(c.w);
+        return r;
+    };
+    const int T = run;
+    const int p0 = (int)((int64_t)rng * T / p.nwg), p1 = (int)((int64_t)(rng + 1) * T / p.nwg);
+
+    int b = 0, qc = 0, hg = 0, part = 0, lp = 0, j = 0;
+    Req rq{};
+    bool more = true;                                  // chunks remain after the current one
+    // next chunk of the batch, in chunk order (query-block group, head group,
+    // part); fields of a new request from LDS while `prologue`, else from memory
+    auto advance = [&](bool prologue) {
+        if (++part == g.NP) {
+            part = 0;
+            if (++hg == g.HG) {
+                hg = 0;
+                ++qc;
+            }
+        }
+        while (qc >= rq.nqcs) {                        // past the request's chunks
+            if (++b >= p.batch) return false;
+            rq = prologue ? req_lds(b) : load_req(p, b);
+            qc = hg = part = 0;
+        }
+        lp = chunk_pages(p, rq, qc, part);
+        return true;
+    };
+    if (p0 < p1) {
+        // the request holding page p0 (the last b with PS[b] <= p0), then the
+        // chunk holding it
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (PS[mid] <= p0) lo = mid; else hi = mid - 1;
+        }
+        b = __builtin_amdgcn_readfirstlane(lo);
+        int off = __builtin_amdgcn_readfirstlane(p0 - PS[b]);
+        rq = req_lds(b);
+        lp = chunk_pages(p, rq, 0, 0);
+        while (more && off >= lp) {
+            off -= lp;
+            more = advance(true);                      // (page p0 exists: stays true)
+        }
+        j = off;
+    }
+    __syncthreads();                                   // the prologue tables are dead
+    const int hc = g.hc;
+    for (int pc = p0; more && pc < p1;) {
+        const int n = min(kRaggedPC, min(lp - j, p1 - pc));
+        int64_t tok0l, tok1l;
+        chunk_tokens(p, rq, qc, part, tok0l, tok1l);
+        const int tok0 = (int)tok0l, ntok = (int)(tok1l - tok0l), h0 = hg * hc;
+        const int qbf = tok0 / p.bsq, qbl = (int)(tok1l - 1) / p.bsq;   // token offsets fit in int
+        const int64_t qrow0 = max((int64_t)rq.q0 + tok0l, (int64_t)0);
+        const int seqc = rq.seqc, pre = rq.pre, row0 = rq.row0;
         PrefillPages pg;
         pg.index_k = p.index_k; pg.k_sp = p.k_sp; pg.k_sb = p.k_sb; pg.P = p.P;
-        pg.bt_row = (slot >= 0 && slot < p.nslots) ? p.bt + (int64_t)slot * p.bt_sr : nullptr;
+        pg.bt_row = (rq.slot >= 0 && rq.slot < p.nslots) ? p.bt + (int64_t)rq.slot * p.bt_sr : nullptr;
         pg.bt_sj = p.bt_sj;
-        pg.j0 = un.y; pg.npg = un.z;
+        pg.j0 = j; pg.npg = n;
         pg.vmin = qb_visible(seqc, pre, qbf, bsq);
         pg.vmax = qb_visible(seqc, pre, qbl, bsq);
         pg.scale = p.scale;
@@ -203,38 +232,56 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
         auto qrow = [&](int col) {
             const int tl = col / hc, hl = col - tl * hc;
             const int t = min(ntok - 1, tl), h = min(p.Hq - 1, h0 + hl);
-            const int64_t row = min((int64_t)p.total_q - 1, (int64_t)qrow0 + t);
+            const int64_t row = min((int64_t)p.total_q - 1, qrow0 + t);
             return p.q + row * p.q_st + (int64_t)h * p.q_sh;
         };
         auto vis = [&](int col) {
             const int tl = col / hc, hl = col - tl * hc;
             if (tl >= ntok || h0 + hl >= p.Hq) return 0;
-            return qb_visible(seqc, pre, (tok0 + tl) / bsq, bsq);
+            return qb_visible(seqc, pre, (tok0 + tl) / p.bsq, bsq);
         };
-        prefill_tile<DI, QT>(pg, qrow, vis, lds);
+        prefill_tile<DI, QT, kRaggedPC>(pg, qrow, vis, lds);
 
         // max over each query block's tokens: output (query block qbf + o /
-        // hc, head h0 + o % hc) x block j0 + pi, S lanes per pair
-        const int npg = pg.npg, O = (qbl - qbf + 1) * hc, NPR = O * npg;
+        // hc, head h0 + o % hc) x block j + pi, S lanes per pair
+        const int O = (qbl - qbf + 1) * hc, NPR = O * n;
         int S = 64;
         while (S > 1 && NPR * S > NT) S >>= 1;
         const int sub = lane & (S - 1);
         for (int pr = tid / S; pr < NPR; pr += NT / S) {
-            const int o = pr / npg, pi = pr - o * npg;
+            const int o = pr / n, pi = pr - o * n;
             const int ql = o / hc, hl = o - ql * hc;
             const int64_t qb = qbf + ql;
             const int t_lo = (int)(max((int64_t)tok0, qb * bsq) - tok0);
             const int t_hi = (int)(min((int64_t)tok0 + ntok, (qb + 1) * bsq) - tok0);
             float m = -INFINITY;
             for (int t = t_lo + sub; t < t_hi; t += S) m = fmaxf(m, lds.sbuf[t * hc + hl][pi]);
-            for (int off = S >> 1; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+            for (int o2 = S >> 1; o2 >= 1; o2 >>= 1) m = fmaxf(m, __shfl_xor(m, o2));
             const int h = h0 + hl;
             const int64_t row = row0 + qb;
             if (sub == 0 && h < p.Hq && row >= 0 && row < p.all_qb)
-                p.ws[(((int64_t)h * p.all_qb + row) * NP + part) * p.MB + pg.j0 + pi] = m;
+                p.ws[(((int64_t)h * p.all_qb + row) * g.NP + part) * p.MB + j + pi] = m;
         }
         __syncthreads();                               // sbuf and the page buffers are reused
+        pc += n;
+        j += n;
+        if (pc < p1 && j == lp) {                      // next chunk that has pages
+            do {
+                more = advance(false);
+            } while (more && lp == 0);
+            j = 0;
+        }
     }
+
+    // owners of the query-block rows: requests rng, rng + nwg, ...; -1 for
+    // the rows past the last request's
+    for (int bb = rng; bb < p.batch; bb += p.nwg) {
+        const int row0 = bb == rng ? ri_row0 : ld(p.cu_qb, p.s_cq, bb);
+        const int rend = bb == rng ? ri_end : ld(p.cu_qb, p.s_cq, bb + 1);
+        for (int r = row0 + tid; r < rend; r += NT)
+            if (r >= 0 && r < p.all_qb) p.rowinfo[r] = bb;
+    }
+    for (int r = max(rows_owned, 0) + rng * NT + tid; r < p.all_qb; r += p.nwg * NT) p.rowinfo[r] = -1;
 }
 
 template <int KPL>
@@ -297,7 +344,7 @@ PrefillGeom prefill_geom(int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, 
     }
     g.HG = (int32_t)((Hq + g.hc - 1) / g.hc);
     g.Cmax = ((all_qb + g.nqc - 1) / g.nqc + batch) * g.HG * g.NP;
-    g.Umax = 2 * g.Cmax * ((MB + kPMaxPC - 1) / kPMaxPC);
+    g.Pmax = g.Cmax * MB;
     return g;
 }
 
@@ -307,35 +354,25 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t prefill_workspace_bytes(int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq) {
     const PrefillGeom g = prefill_geom(batch, Hq, all_qb, MB, bsq);
-    return 256 + align256(4 * (size_t)all_qb) + align256(48 * (size_t)g.Cmax) + align256(16 * (size_t)g.Umax) +
-           align256(4 * (size_t)(Hq * all_qb * g.NP * MB));
+    return align256(4 * (size_t)all_qb) + align256(4 * (size_t)(Hq * all_qb * g.NP * MB));
 }
 
 void prefill_carve_workspace(void *ws, int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq,
                              PrefillSelParams &p) {
     p.g = prefill_geom(batch, Hq, all_qb, MB, bsq);
     uint8_t *b = (uint8_t *)ws;
-    p.hdr = (int32_t *)b;
-    b += 256;
     p.rowinfo = (int32_t *)b;
     b += align256(4 * (size_t)all_qb);
-    p.chunks = (int4 *)b;
-    b += align256(48 * (size_t)p.g.Cmax);
-    p.units = (int4 *)b;
-    b += align256(16 * (size_t)p.g.Umax);
     p.ws = (float *)b;
 }
 
 hipError_t launch_prefill_select(const PrefillSelParams &p, int Di, hipStream_t s) {
     if ((int64_t)p.Hq * p.all_qb == 0) return hipSuccess;
-    hipLaunchKernelGGL(prefill_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     if (Di == 128)
         hipLaunchKernelGGL(prefill_score_ragged_kernel<128>, dim3(p.nwg), dim3(64 * kPWaves), 0, s, p);
     else
         hipLaunchKernelGGL(prefill_score_ragged_kernel<64>, dim3(p.nwg), dim3(64 * kPWaves), 0, s, p);
-    e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (p.MB <= 64) return launch_select<1>(p, s);
     if (p.MB <= 128) return launch_select<2>(p, s);

@@ -1,5 +1,5 @@
 // One prefill score tile on MFMA: up to 512 query columns (bf16 rows of Di)
-// against a run of at most kPMaxPC consecutive logical blocks of one request's
+// against a run of at most MPC consecutive logical blocks of one request's
 // FP8 index pages, reduced to the per-(column, block) maximum of the dot
 // products over the keys the column sees.  Shared by the prefill path of
 // msa_block_score (columns = query tokens of one row) and by the ragged
@@ -26,7 +26,7 @@
 namespace msa {
 
 constexpr int kPWaves = 8;        // waves per workgroup, two per SIMD
-constexpr int kPMaxPC = 8;        // blocks per tile, at most
+constexpr int kPMaxPC = 8;        // blocks per tile of the prefill score sheet, at most
 
 // max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
 // first, unlike fmaxf); the operands are dot products, never NaN (a NaN dot
@@ -64,12 +64,14 @@ __device__ __forceinline__ void prefill_mma(const uint4 (&a)[DI / 32], const uin
                 __builtin_bit_cast(bf16x8, a[ks]), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
 }
 
-// LDS of one tile: two pairs of bf16 page buffers and the block maxima.
-template <int DI, int QT>
+// LDS of one tile of at most MPC blocks: two pairs of bf16 page buffers and
+// the block maxima.
+template <int DI, int QT, int MPC>
 struct PrefillLds {
     static constexpr int PQ = 16 * QT * kPWaves;    // query columns
+    static constexpr int MaxPages = MPC;
     __attribute__((aligned(16))) uint8_t kb[4][kBlock * DI * 2];
-    float sbuf[PQ][kPMaxPC + 1];
+    float sbuf[PQ][MPC + 1];
 };
 
 // The pages of a tile: blocks j0 .. j0+npg-1 of a request whose block table
@@ -80,7 +82,7 @@ struct PrefillPages {
     int P;
     const int32_t *bt_row;
     int64_t bt_sj;
-    int j0, npg;              // npg <= kPMaxPC
+    int j0, npg;              // npg <= the tile's MPC (< 64)
     int vmin, vmax;           // keys seen by every column, by the column that sees most
     float scale;
 };
@@ -92,9 +94,9 @@ struct PrefillPages {
 // query row (any valid address for columns that are not used), vis(col) the
 // number of keys the column sees (0 for unused columns).  Every thread of the
 // workgroup calls it; it ends with a barrier, after which sbuf is complete.
-template <int DI, int QT, class QRow, class Vis>
+template <int DI, int QT, int MPC, class QRow, class Vis>
 __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, Vis vis,
-                                             PrefillLds<DI, QT> &lds) {
+                                             PrefillLds<DI, QT, MPC> &lds) {
     constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
     constexpr int NT = 64 * kPWaves;            // threads per workgroup
     constexpr int RB = DI * 2;                  // bytes per bf16 row (query or key)
@@ -102,7 +104,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
     constexpr int VPT = kBlock * DI / (16 * NT) > 0 ? kBlock * DI / (16 * NT) : 1;  // 16-byte FP8 loads per slice
     constexpr int TPK = DI / (16 * VPT);        // slices per key row
     constexpr int NLD = TPK * kBlock;           // threads holding a slice (whole waves)
-    constexpr int PQ = PrefillLds<DI, QT>::PQ;
+    constexpr int PQ = PrefillLds<DI, QT, MPC>::PQ;
+    static_assert(MPC < 64, "page ids live one per lane");
     static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
     static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the first pair");
 
@@ -111,7 +114,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
     const int grp = lane >> 4, li = lane & 15;
     const int j0 = pg.j0, npg = pg.npg, vmin = pg.vmin, vmax = pg.vmax;
 
-    // page table of the tile: lane i holds block j0 + i (npg <= 8 < 64)
+    // page table of the tile: lane i holds block j0 + i (npg < 64)
     const int pid_l = (lane < npg && pg.bt_row) ? pg.bt_row[(int64_t)(j0 + lane) * pg.bt_sj] : -1;
     const bool vis_l = lane < npg && (j0 + lane) * kBlock < vmax;
     const bool ok_l = pid_l >= 0 && pid_l < pg.P;

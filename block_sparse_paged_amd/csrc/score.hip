@@ -222,8 +222,8 @@ template <int DI, int QT>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void score_prefill_kernel(ScoreParams p, int WPC) {
     constexpr int NT = 64 * kPWaves;            // threads per workgroup
-    constexpr int PQ = PrefillLds<DI, QT>::PQ;  // query tokens per workgroup
-    __shared__ PrefillLds<DI, QT> lds;
+    constexpr int PQ = PrefillLds<DI, QT, kPMaxPC>::PQ;  // query tokens per workgroup
+    __shared__ PrefillLds<DI, QT, kPMaxPC> lds;
 
     const int tid = threadIdx.x;
     const int QC = (p.T + PQ - 1) / PQ;
@@ -264,7 +264,7 @@ void score_prefill_kernel(ScoreParams p, int WPC) {
         const int t = tq0 + col;
         return t < p.T ? max(0, L - (p.T - 1 - t)) : 0;
     };
-    prefill_tile<DI, QT>(pg, qrow, vis, lds);
+    prefill_tile<DI, QT, kPMaxPC>(pg, qrow, vis, lds);
 
     const int npg = pg.npg, j0 = pg.j0;
     for (int idx = tid; idx < (tq1 - tq0) * npg; idx += NT) {
