@@ -111,6 +111,8 @@ __device__ __forceinline__ int chunk_pages(const PrefillSelParams &p, const Req 
 constexpr int kRaggedPC = 14;
 // requests whose fields the prologue keeps in LDS (larger batches re-read them)
 constexpr int kLdsReqs = 512;
+// the fixed cost of a tile (queries and first pages on their way), in pages
+constexpr int kRampWeight = 3;
 
 template <int DI>
 __global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -132,8 +134,11 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
     const int ri_end = rng < p.batch ? ld(p.cu_qb, p.s_cq, rng + 1) : 0;
     const int rows_owned = ld(p.cu_qb, p.s_cq, p.batch);
 
-    // pages of every request, prefix-summed into PS, and the request fields
-    // for small batches, in the page buffers (before any page is staged)
+    // weight of every request, prefix-summed into PS, and the request fields
+    // for small batches, in the page buffers (before any page is staged).  A
+    // chunk with pages weighs its pages plus kRampWeight, the cost of loading
+    // its queries and first pages: shares that start a new chunk hold fewer
+    // pages.
     int *PS = (int *)&lds.kb[0][0];
     int *RQ = PS + ((kPlanMaxBatch + 4) & ~3);          // 16-byte aligned
     const bool rq_lds = p.batch <= kLdsReqs;
@@ -144,7 +149,10 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
         if (b < p.batch) {
             const Req r = load_req(p, b);
             for (int qc = 0; qc < r.nqcs; ++qc)
-                for (int part = 0; part < g.NP; ++part) n += chunk_pages(p, r, qc, part);
+                for (int part = 0; part < g.NP; ++part) {
+                    const int l = chunk_pages(p, r, qc, part);
+                    n += l ? l + kRampWeight : 0;
+                }
             n *= g.HG;
             if (rq_lds) {
                 *(int4 *)(RQ + 8 * b) = make_int4(r.q0, r.nq, r.nqb, r.row0);
@@ -167,15 +175,63 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
         r.slot = __builtin_amdgcn_readfirstlane(c.z); r.nqcs = __builtin_amdgcn_readfirstlane(c.w);
         return r;
     };
-    const int T = run;
-    const int p0 = (int)((int64_t)rng * T / p.nwg), p1 = (int)((int64_t)(rng + 1) * T / p.nwg);
-
+    // The share is the weight range [w0, w1).  A weight position w falls in
+    // the chunk whose range [cum, cum + pages + kRampWeight) holds it, at page
+    // max(0, w - cum - kRampWeight); the share takes the pages from the
+    // position of w0 up to that of w1, so every page goes to exactly one share.
+    const int W = run;
+    const int w0 = (int)((int64_t)rng * W / p.nwg), w1 = (int)((int64_t)(rng + 1) * W / p.nwg);
+    const int per_qc = g.HG * g.NP;                    // chunks per query-block group
     int b = 0, qc = 0, hg = 0, part = 0, lp = 0, j = 0;
+    int cum = 0;                                       // weight position of the current chunk
     Req rq{};
-    bool more = true;                                  // chunks remain after the current one
+    bool have = false;                                 // a current chunk
+    if (w0 < w1) {
+        // the request holding w0 (the last b with PS[b] <= w0), then its chunk
+        // holding w0: the request's chunk weights prefix-summed across a wave,
+        // 64 chunks at a time
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (PS[mid] <= w0) lo = mid; else hi = mid - 1;
+        }
+        b = __builtin_amdgcn_readfirstlane(lo);
+        const int psb = __builtin_amdgcn_readfirstlane(PS[b]);
+        const int off = w0 - psb;
+        rq = req_lds(b);
+        const int nch = rq.nqcs * per_qc;
+        int base = 0;
+        for (int kb = 0; kb < nch; kb += 64) {
+            const int k = kb + lane;
+            int wt = 0;
+            if (k < nch) {
+                const int l = chunk_pages(p, rq, k / per_qc, k % g.NP);
+                wt = l ? l + kRampWeight : 0;
+            }
+            const int inc = wave_prefix_sum(wt);
+            const uint64_t m = __ballot(k < nch && base + inc > off);
+            if (m) {
+                const int L = __builtin_ctzll(m);
+                const int k0 = kb + L;
+                qc = k0 / per_qc;
+                hg = (k0 - qc * per_qc) / g.NP;
+                part = k0 % g.NP;
+                cum = psb + base + __builtin_amdgcn_readlane(inc - wt, L);
+                have = true;
+                break;
+            }
+            base += __builtin_amdgcn_readlane(inc, 63);
+        }
+        if (have) {
+            lp = chunk_pages(p, rq, qc, part);
+            j = max(0, w0 - cum - kRampWeight);
+        }
+    }
+    __syncthreads();                                   // the prologue tables are dead
+
     // next chunk of the batch, in chunk order (query-block group, head group,
-    // part); fields of a new request from LDS while `prologue`, else from memory
-    auto advance = [&](bool prologue) {
+    // part)
+    auto advance = [&]() {
         if (++part == g.NP) {
             part = 0;
             if (++hg == g.HG) {
@@ -185,92 +241,77 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
         }
         while (qc >= rq.nqcs) {                        // past the request's chunks
             if (++b >= p.batch) return false;
-            rq = prologue ? req_lds(b) : load_req(p, b);
+            rq = load_req(p, b);
             qc = hg = part = 0;
         }
         lp = chunk_pages(p, rq, qc, part);
         return true;
     };
-    if (p0 < p1) {
-        // the request holding page p0 (the last b with PS[b] <= p0), then the
-        // chunk holding it
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (PS[mid] <= p0) lo = mid; else hi = mid - 1;
-        }
-        b = __builtin_amdgcn_readfirstlane(lo);
-        int off = __builtin_amdgcn_readfirstlane(p0 - PS[b]);
-        rq = req_lds(b);
-        lp = chunk_pages(p, rq, 0, 0);
-        while (more && off >= lp) {
-            off -= lp;
-            more = advance(true);                      // (page p0 exists: stays true)
-        }
-        j = off;
-    }
-    __syncthreads();                                   // the prologue tables are dead
     const int hc = g.hc;
-    for (int pc = p0; more && pc < p1;) {
-        const int n = min(kRaggedPC, min(lp - j, p1 - pc));
-        int64_t tok0l, tok1l;
-        chunk_tokens(p, rq, qc, part, tok0l, tok1l);
-        const int tok0 = (int)tok0l, ntok = (int)(tok1l - tok0l), h0 = hg * hc;
-        const int qbf = tok0 / p.bsq, qbl = (int)(tok1l - 1) / p.bsq;   // token offsets fit in int
-        const int64_t qrow0 = max((int64_t)rq.q0 + tok0l, (int64_t)0);
-        const int seqc = rq.seqc, pre = rq.pre, row0 = rq.row0;
-        PrefillPages pg;
-        pg.index_k = p.index_k; pg.k_sp = p.k_sp; pg.k_sb = p.k_sb; pg.P = p.P;
-        pg.bt_row = (rq.slot >= 0 && rq.slot < p.nslots) ? p.bt + (int64_t)rq.slot * p.bt_sr : nullptr;
-        pg.bt_sj = p.bt_sj;
-        pg.j0 = j; pg.npg = n;
-        pg.vmin = qb_visible(seqc, pre, qbf, bsq);
-        pg.vmax = qb_visible(seqc, pre, qbl, bsq);
-        pg.scale = p.scale;
-        // column col = (token tok0 + col / hc, head h0 + col % hc); columns
-        // past the chunk read its last valid row and see no key
-        auto qrow = [&](int col) {
-            const int tl = col / hc, hl = col - tl * hc;
-            const int t = min(ntok - 1, tl), h = min(p.Hq - 1, h0 + hl);
-            const int64_t row = min((int64_t)p.total_q - 1, qrow0 + t);
-            return p.q + row * p.q_st + (int64_t)h * p.q_sh;
-        };
-        auto vis = [&](int col) {
-            const int tl = col / hc, hl = col - tl * hc;
-            if (tl >= ntok || h0 + hl >= p.Hq) return 0;
-            return qb_visible(seqc, pre, (tok0 + tl) / p.bsq, bsq);
-        };
-        prefill_tile<DI, QT, kRaggedPC>(pg, qrow, vis, lds);
+    while (have) {
+        const int wt = lp + kRampWeight;               // lp > 0 here
+        const bool last = w1 <= cum + wt;              // the share ends in this chunk
+        const int jend = last ? min(lp, max(0, w1 - cum - kRampWeight)) : lp;
+        for (; j < jend;) {
+            const int n = min(kRaggedPC, jend - j);
+            int64_t tok0l, tok1l;
+            chunk_tokens(p, rq, qc, part, tok0l, tok1l);
+            const int tok0 = (int)tok0l, ntok = (int)(tok1l - tok0l), h0 = hg * hc;
+            const int qbf = tok0 / p.bsq, qbl = (int)(tok1l - 1) / p.bsq;   // token offsets fit in int
+            const int64_t qrow0 = max((int64_t)rq.q0 + tok0l, (int64_t)0);
+            const int seqc = rq.seqc, pre = rq.pre, row0 = rq.row0;
+            PrefillPages pg;
+            pg.index_k = p.index_k; pg.k_sp = p.k_sp; pg.k_sb = p.k_sb; pg.P = p.P;
+            pg.bt_row = (rq.slot >= 0 && rq.slot < p.nslots) ? p.bt + (int64_t)rq.slot * p.bt_sr : nullptr;
+            pg.bt_sj = p.bt_sj;
+            pg.j0 = j; pg.npg = n;
+            pg.vmin = qb_visible(seqc, pre, qbf, bsq);
+            pg.vmax = qb_visible(seqc, pre, qbl, bsq);
+            pg.scale = p.scale;
+            // column col = (token tok0 + col / hc, head h0 + col % hc); columns
+            // past the chunk read its last valid row and see no key
+            auto qrow = [&](int col) {
+                const int tl = col / hc, hl = col - tl * hc;
+                const int t = min(ntok - 1, tl), h = min(p.Hq - 1, h0 + hl);
+                const int64_t row = min((int64_t)p.total_q - 1, qrow0 + t);
+                return p.q + row * p.q_st + (int64_t)h * p.q_sh;
+            };
+            auto vis = [&](int col) {
+                const int tl = col / hc, hl = col - tl * hc;
+                if (tl >= ntok || h0 + hl >= p.Hq) return 0;
+                return qb_visible(seqc, pre, (tok0 + tl) / p.bsq, bsq);
+            };
+            prefill_tile<DI, QT, kRaggedPC>(pg, qrow, vis, lds);
 
-        // max over each query block's tokens: output (query block qbf + o /
-        // hc, head h0 + o % hc) x block j + pi, S lanes per pair
-        const int O = (qbl - qbf + 1) * hc, NPR = O * n;
-        int S = 64;
-        while (S > 1 && NPR * S > NT) S >>= 1;
-        const int sub = lane & (S - 1);
-        for (int pr = tid / S; pr < NPR; pr += NT / S) {
-            const int o = pr / n, pi = pr - o * n;
-            const int ql = o / hc, hl = o - ql * hc;
-            const int64_t qb = qbf + ql;
-            const int t_lo = (int)(max((int64_t)tok0, qb * bsq) - tok0);
-            const int t_hi = (int)(min((int64_t)tok0 + ntok, (qb + 1) * bsq) - tok0);
-            float m = -INFINITY;
-            for (int t = t_lo + sub; t < t_hi; t += S) m = fmaxf(m, lds.sbuf[t * hc + hl][pi]);
-            for (int o2 = S >> 1; o2 >= 1; o2 >>= 1) m = fmaxf(m, __shfl_xor(m, o2));
-            const int h = h0 + hl;
-            const int64_t row = row0 + qb;
-            if (sub == 0 && h < p.Hq && row >= 0 && row < p.all_qb)
-                p.ws[(((int64_t)h * p.all_qb + row) * g.NP + part) * p.MB + j + pi] = m;
+            // max over each query block's tokens: output (query block qbf + o /
+            // hc, head h0 + o % hc) x block j + pi, S lanes per pair
+            const int O = (qbl - qbf + 1) * hc, NPR = O * n;
+            int S = 64;
+            while (S > 1 && NPR * S > NT) S >>= 1;
+            const int sub = lane & (S - 1);
+            for (int pr = tid / S; pr < NPR; pr += NT / S) {
+                const int o = pr / n, pi = pr - o * n;
+                const int ql = o / hc, hl = o - ql * hc;
+                const int64_t qb = qbf + ql;
+                const int t_lo = (int)(max((int64_t)tok0, qb * bsq) - tok0);
+                const int t_hi = (int)(min((int64_t)tok0 + ntok, (qb + 1) * bsq) - tok0);
+                float m = -INFINITY;
+                for (int t = t_lo + sub; t < t_hi; t += S) m = fmaxf(m, lds.sbuf[t * hc + hl][pi]);
+                for (int o2 = S >> 1; o2 >= 1; o2 >>= 1) m = fmaxf(m, __shfl_xor(m, o2));
+                const int h = h0 + hl;
+                const int64_t row = row0 + qb;
+                if (sub == 0 && h < p.Hq && row >= 0 && row < p.all_qb)
+                    p.ws[(((int64_t)h * p.all_qb + row) * g.NP + part) * p.MB + j + pi] = m;
+            }
+            __syncthreads();                               // sbuf and the page buffers are reused
+            j += n;
         }
-        __syncthreads();                               // sbuf and the page buffers are reused
-        pc += n;
-        j += n;
-        if (pc < p1 && j == lp) {                      // next chunk that has pages
-            do {
-                more = advance(false);
-            } while (more && lp == 0);
-            j = 0;
-        }
+        if (last) break;
+        cum += wt;                                     // next chunk that has pages
+        do {
+            have = advance();
+        } while (have && lp == 0);
+        j = 0;
     }
 
     // owners of the query-block rows: requests rng, rng + nwg, ...; -1 for
