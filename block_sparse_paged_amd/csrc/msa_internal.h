@@ -88,7 +88,9 @@ struct PrefillSelParams {
     float scale;
     PrefillGeom g;
     int32_t nwg;                                       // workgroups of the scoring launch (multiple of 8)
+    int32_t fused;                                     // selection inside the scoring launch
     // workspace (msa_prefill_block_score_workspace_bytes)
+    int32_t *counters;  // [Hq, all_qb] arrival counters (zero between calls)
     int32_t *rowinfo;   // [all_qb]: request owning the query-block row, or -1
     float *ws;          // [Hq, all_qb, NP, MB] query-block maxima
 };

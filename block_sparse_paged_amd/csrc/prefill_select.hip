@@ -46,6 +46,16 @@ __device__ __forceinline__ int qb_visible(int seqc, int pre, int64_t qb, int64_t
 
 __device__ __forceinline__ int ld(const int32_t *a, int64_t s, int64_t i) { return a[i * s]; }
 
+// the query-block sheet is written and read with device-coherent (agent
+// scope) accesses: the workgroup that selects a group's rows reads what the
+// other workgroups of the launch wrote, possibly on another XCD
+__device__ __forceinline__ void st_sheet(float *a, float v) {
+    __hip_atomic_store((uint32_t *)a, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_sheet(const float *a) {
+    return __uint_as_float(__hip_atomic_load((const uint32_t *)a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // exclusive prefix sum over the NT threads of the workgroup; total gets the
 // sum of all.  wsum: NT/64 ints of LDS.
 template <int NT>
@@ -104,6 +114,47 @@ __device__ __forceinline__ int chunk_pages(const PrefillSelParams &p, const Req 
     if (tok0 >= min((int64_t)r.nq, (int64_t)r.nqb * bsq)) return 0;
     const int qbl = p.g.NP > 1 ? qc : min(r.nqb - 1, (qc + 1) * p.g.nqc - 1);
     return (qb_visible(r.seqc, r.pre, qbl, bsq) + kBlock - 1) / kBlock;
+}
+
+// The selection of row (head h, query block qb of request r, out_topk row g)
+// from the query-block sheet: forced blocks become the largest keys, the other
+// candidates their score keys, and the wave-level radix select takes topk.
+// The sheet is read with device-coherent loads (it may have been written by
+// other workgroups of the same launch).
+template <int KPL>
+__device__ __forceinline__ void select_prefill_row(const PrefillSelParams &p, const Req &r, int h, int g, int qb,
+                                                   int *hist) {
+    const int lane = threadIdx.x & 63;
+    const int64_t bsq = p.bsq;
+    int32_t *dst = p.out + (int64_t)h * p.o_sh + (int64_t)g * p.o_sq;
+    const int V = qb_visible(r.seqc, r.pre, qb, bsq);
+    const int ncand = (V + kBlock - 1) / kBlock;
+    // parts of the query block that hold tokens (more than one only when
+    // block_size_q exceeds a chunk)
+    const int64_t ntq = min(bsq, (int64_t)r.nq - qb * bsq);
+    const int npv = max(1, min(p.g.NP, (int)((ntq + kPrefillCols - 1) / kPrefillCols)));
+    const float *src = p.ws + ((int64_t)h * p.all_qb + g) * p.g.NP * p.MB;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const int j = i * 64 + lane;
+        key[i] = 0u;
+        if (j < ncand) {
+            float s = ld_sheet(src + j);
+            for (int q = 1; q < npv; ++q) s = fmaxf(s, ld_sheet(src + (int64_t)q * p.MB + j));
+            const bool forced = j < p.init_blocks || j >= ncand - p.local_blocks;
+            key[i] = forced ? 0xffffffffu : score_key(s);
+        }
+    }
+    select_keys<KPL>(key, p.topk, hist, [&](int pos, int id) { dst[(int64_t)pos * p.o_si] = id; });
+}
+
+// out_topk rows of query block qb of request r for heads [h0, h1): -1
+__device__ __forceinline__ void fill_rows_none(const PrefillSelParams &p, int g, int h0, int h1, int tid, int nt) {
+    for (int i = tid; i < (h1 - h0) * p.topk; i += nt) {
+        const int h = h0 + i / p.topk, k = i - (i / p.topk) * p.topk;
+        p.out[(int64_t)h * p.o_sh + (int64_t)g * p.o_sq + (int64_t)k * p.o_si] = -1;
+    }
 }
 
 // blocks per scoring tile: as many as LDS holds next to the four page
@@ -186,7 +237,9 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
     int cum = 0;                                       // weight position of the current chunk
     Req rq{};
     bool have = false;                                 // a current chunk
-    if (w0 < w1) {
+    // (a share with no weight still locates the chunk at its position: it
+    // arrives at that chunk's group without work, see below)
+    if (w0 < W) {
         // the request holding w0 (the last b with PS[b] <= w0), then its chunk
         // holding w0: the request's chunk weights prefix-summed across a wave,
         // 64 chunks at a time
@@ -248,6 +301,56 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
         return true;
     };
     const int hc = g.hc;
+    // Selection inside the launch (p.fused): a group (request, query-block
+    // group, head group) is done when every share whose weight range meets
+    // the group's has written its pages' maxima; each such share then adds
+    // one to the group's counter, and the one that completes the count
+    // selects the group's rows and clears the counter.  The number of such
+    // shares follows from the weight positions alone: the shares whose range
+    // starts inside [g0w, g1w), plus the one that holds g0w when g0w is not
+    // a share start.
+    auto seg_count = [&](int g0w, int g1w) {
+        const int64_t n = p.nwg;
+        const int64_t c0 = ((int64_t)g0w * n + W - 1) / W, c1 = ((int64_t)g1w * n + W - 1) / W;
+        const bool start = c0 < n && (c0 * W / n) == g0w;
+        return (int)(c1 - c0) + (start ? 0 : 1);
+    };
+    // weight range of the current chunk's group (its NP parts are
+    // consecutive chunks)
+    auto group_span = [&](int &g0w, int &g1w) {
+        int before = 0, from = 0;
+        for (int pp = 0; pp < g.NP; ++pp) {
+            const int l = chunk_pages(p, rq, qc, pp);
+            const int w = l ? l + kRampWeight : 0;
+            if (pp < part) before += w; else from += w;
+        }
+        g0w = cum - before;
+        g1w = cum + from;
+    };
+    __shared__ int s_last;
+    auto arrive = [&](const Req &gr, int gqc, int ghg, int g0w, int g1w) {
+        const int grow0 = gr.row0 + gqc * g.nqc;       // the group's first out_topk row
+        if (grow0 < 0 || grow0 >= p.all_qb) return;   // (inconsistent offsets: nothing to select)
+        const int gh0 = ghg * hc;
+        int *ctr = p.counters + (int64_t)gh0 * p.all_qb + grow0;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's sheet stores are done
+        __syncthreads();
+        if (tid == 0)
+            s_last = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                     seg_count(g0w, g1w) - 1;
+        __syncthreads();
+        if (!s_last) return;
+        const int wave = tid >> 6;
+        const int qb0 = gqc * g.nqc, nqbg = min(gr.nqb, qb0 + g.nqc) - qb0;
+        const int nh = min(p.Hq, gh0 + hc) - gh0;
+        int *hist = (int *)&lds.kb[0][0] + 256 * wave;   // the page buffers are idle here
+        for (int i = wave; i < nqbg * nh; i += kPWaves) {
+            const int ql = i / nh, h = gh0 + (i - ql * nh);
+            if (grow0 + ql < p.all_qb) select_prefill_row<2>(p, gr, h, grow0 + ql, qb0 + ql, hist);
+        }
+        if (tid == 0) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                               // the page buffers are reused
+    };
     while (have) {
         const int wt = lp + kRampWeight;               // lp > 0 here
         const bool last = w1 <= cum + wt;              // the share ends in this chunk
@@ -301,17 +404,26 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
                 const int h = h0 + hl;
                 const int64_t row = row0 + qb;
                 if (sub == 0 && h < p.Hq && row >= 0 && row < p.all_qb)
-                    p.ws[(((int64_t)h * p.all_qb + row) * g.NP + part) * p.MB + j + pi] = m;
+                    st_sheet(p.ws + (((int64_t)h * p.all_qb + row) * g.NP + part) * p.MB + j + pi, m);
             }
             __syncthreads();                               // sbuf and the page buffers are reused
             j += n;
         }
-        if (last) break;
+        int g0w = 0, g1w = 0;
+        if (p.fused) group_span(g0w, g1w);
+        if (last) {
+            if (p.fused) arrive(rq, qc, hg, g0w, g1w);
+            break;
+        }
+        const Req grq = rq;
+        const int gb = b, gqc = qc, ghg = hg;
         cum += wt;                                     // next chunk that has pages
         do {
             have = advance();
         } while (have && lp == 0);
         j = 0;
+        if (p.fused && (!have || b != gb || qc != gqc || hg != ghg))   // left the group
+            arrive(grq, gqc, ghg, g0w, g1w);
     }
 
     // owners of the query-block rows: requests rng, rng + nwg, ...; -1 for
@@ -323,6 +435,20 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
             if (r >= 0 && r < p.all_qb) p.rowinfo[r] = bb;
     }
     for (int r = max(rows_owned, 0) + rng * NT + tid; r < p.all_qb; r += p.nwg * NT) p.rowinfo[r] = -1;
+    if (!p.fused) return;
+    // rows that no share selects: groups without pages (every query block
+    // sees no key) and rows past the last request's
+    for (int bb = rng; bb < p.batch; bb += p.nwg) {
+        const Req r = load_req(p, bb);
+        for (int gq = 0; gq < r.nqcs; ++gq) {
+            int w = 0;
+            for (int pp = 0; pp < g.NP; ++pp) w += chunk_pages(p, r, gq, pp);
+            if (w) continue;
+            for (int q = gq * g.nqc; q < min(r.nqb, gq * g.nqc + g.nqc); ++q)
+                if (r.row0 + q >= 0 && r.row0 + q < p.all_qb) fill_rows_none(p, r.row0 + q, 0, p.Hq, tid, NT);
+        }
+    }
+    for (int r = max(rows_owned, 0) + rng; r < p.all_qb; r += p.nwg) fill_rows_none(p, r, 0, p.Hq, tid, NT);
 }
 
 template <int KPL>
@@ -332,36 +458,13 @@ __global__ __launch_bounds__(256) void prefill_select_kernel(PrefillSelParams p)
     const int64_t rowid = (int64_t)blockIdx.x * 4 + wave;
     if (rowid >= (int64_t)p.Hq * p.all_qb) return;    // no barriers in this kernel
     const int h = (int)(rowid / p.all_qb), g = (int)(rowid - (int64_t)h * p.all_qb);
-    int32_t *dst = p.out + (int64_t)h * p.o_sh + (int64_t)g * p.o_sq;
     const int b = p.rowinfo[g];
-    if (b < 0) {
-        for (int i = lane; i < p.topk; i += 64) dst[(int64_t)i * p.o_si] = -1;
+    if (b < 0 || b >= p.batch) {
+        fill_rows_none(p, g, h, h + 1, lane, 64);
         return;
     }
-    const int64_t bsq = p.bsq;
-    const int qb = g - ld(p.cu_qb, p.s_cq, b);
-    const int nq = ld(p.cu_seqlens, p.s_cu, b + 1) - ld(p.cu_seqlens, p.s_cu, b);
-    const int seqc = min(max(ld(p.seq_lens, p.s_sl, b), 0), p.MB * kBlock);
-    const int V = qb_visible(seqc, ld(p.prefix_lens, p.s_pl, b), qb, bsq);
-    const int ncand = (V + kBlock - 1) / kBlock;
-    // parts of the query block that hold tokens (more than one only when
-    // block_size_q exceeds a chunk)
-    const int64_t ntq = min(bsq, (int64_t)nq - qb * bsq);
-    const int npv = max(1, min(p.g.NP, (int)((ntq + kPrefillCols - 1) / kPrefillCols)));
-    const float *src = p.ws + ((int64_t)h * p.all_qb + g) * p.g.NP * p.MB;
-    uint32_t key[KPL];
-#pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int j = i * 64 + lane;
-        key[i] = 0u;
-        if (j < ncand) {
-            float s = src[j];
-            for (int q = 1; q < npv; ++q) s = fmaxf(s, src[(int64_t)q * p.MB + j]);
-            const bool forced = j < p.init_blocks || j >= ncand - p.local_blocks;
-            key[i] = forced ? 0xffffffffu : score_key(s);
-        }
-    }
-    select_keys<KPL>(key, p.topk, hist[wave], [&](int pos, int id) { dst[(int64_t)pos * p.o_si] = id; });
+    const Req r = load_req(p, b);
+    select_prefill_row<KPL>(p, r, h, g, g - r.row0, hist[wave]);
 }
 
 template <int KPL>
@@ -395,13 +498,19 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t prefill_workspace_bytes(int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq) {
     const PrefillGeom g = prefill_geom(batch, Hq, all_qb, MB, bsq);
-    return align256(4 * (size_t)all_qb) + align256(4 * (size_t)(Hq * all_qb * g.NP * MB));
+    return align256(4 * (size_t)(Hq * all_qb)) + align256(4 * (size_t)all_qb) +
+           align256(4 * (size_t)(Hq * all_qb * g.NP * MB));
 }
 
 void prefill_carve_workspace(void *ws, int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, int64_t bsq,
                              PrefillSelParams &p) {
     p.g = prefill_geom(batch, Hq, all_qb, MB, bsq);
+    // selection inside the scoring launch when a group's rows fit a few
+    // selections per wave and a score row fits two keys per lane
+    p.fused = MB <= 128 && (int64_t)p.g.nqc * p.g.hc <= 4 * kPWaves;
     uint8_t *b = (uint8_t *)ws;
+    p.counters = (int32_t *)b;
+    b += align256(4 * (size_t)(Hq * all_qb));
     p.rowinfo = (int32_t *)b;
     b += align256(4 * (size_t)all_qb);
     p.ws = (float *)b;
@@ -414,7 +523,7 @@ hipError_t launch_prefill_select(const PrefillSelParams &p, int Di, hipStream_t 
     else
         hipLaunchKernelGGL(prefill_score_ragged_kernel<64>, dim3(p.nwg), dim3(64 * kPWaves), 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || p.fused) return e;
     if (p.MB <= 64) return launch_select<1>(p, s);
     if (p.MB <= 128) return launch_select<2>(p, s);
     if (p.MB <= 256) return launch_select<4>(p, s);

@@ -224,10 +224,11 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Workspace bytes msa_prefill_block_score needs: its plan (chunk and unit
- * tables, the owner of every query-block row) and the query-block score sheet
- * [num_q_heads, all_seqblock_q, parts, max_blocks] f32, parts = 1 unless
- * block_size_q > 512.  Depends on these sizes only; 0 for sizes out of range.
+ * Workspace bytes msa_prefill_block_score needs: one arrival counter per
+ * output row, the owner of every query-block row and the query-block score
+ * sheet [num_q_heads, all_seqblock_q, parts, max_blocks] f32, parts = 1
+ * unless block_size_q > 512.  Depends on these sizes only; 0 for sizes out of
+ * range.
  */
 size_t msa_prefill_block_score_workspace_bytes(int32_t batch, int32_t num_q_heads,
                                                int32_t all_seqblock_q, int32_t max_blocks,
@@ -255,7 +256,10 @@ size_t msa_prefill_block_score_workspace_bytes(int32_t batch, int32_t num_q_head
  *             at most topk), then the other candidates by score (ties to the
  *             lower id), up to topk in all; ascending ids, padded with -1.
  * Rows of out_topk that no request owns are all -1.  FP8 codes are decoded
- * exactly, products run on bf16 MFMA tiles with fp32 sums.
+ * exactly, products run on bf16 MFMA tiles with fp32 sums.  With MB <= 128
+ * and at most 32 rows per work group (query blocks of at least 16 tokens x
+ * heads) the selection runs inside the scoring launch; otherwise a selection
+ * launch follows it.
  *
  *   q              [total_q, Hq, Di]  bf16   innermost stride 1, 16-byte aligned rows
  *   index_k        [P, 128, Di]       fp8e4m3fn  one index head; rows 16-byte aligned
@@ -268,9 +272,10 @@ size_t msa_prefill_block_score_workspace_bytes(int32_t batch, int32_t num_q_head
  *                  all_seqblock_q >= cu_seqblocks_q[batch]
  *   workspace      at least msa_prefill_block_score_workspace_bytes(batch, Hq,
  *                  all_seqblock_q, MB, block_size_q) bytes, 256-byte aligned,
- *                  owned by the caller; needs no initialisation (each call
- *                  writes what it reads).  Calls sharing a workspace must not
- *                  run concurrently.
+ *                  owned by the caller.  Zero-fill it once before its first
+ *                  use; every call leaves its counters at zero again, so it is
+ *                  reused (and graph-replayed) without clearing.  Calls sharing
+ *                  a workspace must not run concurrently.
  * Di must be 64 or 128; batch at most 8192.  The page-size and length hints
  * of the pages' signature (max_seqlen_q/k, max_seqblock_q) are not needed:
  * the call plans its work on the device.  Inputs outside this contract

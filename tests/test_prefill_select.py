@@ -36,12 +36,11 @@ def upload(pb):
     return d
 
 
-def prefill_workspace(msa, pb, fill=0x5A):
+def prefill_workspace(msa, pb):
     n = msa.msa_prefill_block_score_workspace_bytes(pb.batch, pb.Hq, pb.all_qb, pb.MB,
                                                     pb.block_size_q)
     assert n > 0 and n % 256 == 0
-    # garbage: the call must not rely on the workspace's contents
-    return torch.full((n,), fill, dtype=torch.uint8, device="cuda")
+    return torch.zeros((n,), dtype=torch.uint8, device="cuda")    # zero-filled once
 
 
 def run(msa, pb, d, ws=None, out=None):
@@ -196,8 +195,51 @@ def test_prefill_select_deterministic(msa):
                              block_size_q=64, topk=8, init_blocks=1, local_blocks=2, seed=4304)
     d = upload(pb)
     a = run(msa, pb, d)
-    b = run(msa, pb, d, ws=prefill_workspace(msa, pb, fill=0xC3))
-    assert torch.equal(a, b)
+    ws = prefill_workspace(msa, pb)
+    b = run(msa, pb, d, ws=ws)
+    c = run(msa, pb, d, ws=ws)                            # the counters are back at zero
+    assert torch.equal(a, b) and torch.equal(a, c)
+
+
+def test_prefill_select_graph_replay(msa):
+    """The call captured in a graph and replayed several times, with eager
+    work and new input values between the replays: every replay matches the
+    eager call on the same inputs (the arrival counters are left at zero)."""
+    pb = synth.prefill_batch("graph", new_tokens=[300, 130], prefix=[2000, 500], Hq=4, Di=128,
+                             block_size_q=64, topk=6, init_blocks=1, local_blocks=1, seed=4306)
+    d = upload(pb)
+    ws = prefill_workspace(msa, pb)
+    out = poisoned((pb.Hq, pb.all_qb, pb.topk), torch.int32)
+    stream = torch.cuda.Stream()
+
+    def call():
+        msa.msa_prefill_block_score(d["q"], d["index_k"], d["block_table"], d["slot_ids"],
+                                    d["cu_seqlens"], d["seq_lens"], d["prefix_lens"],
+                                    pb.block_size_q, pb.B, pb.topk, pb.init_blocks,
+                                    pb.local_blocks, pb.scale, d["cu_seqblocks_q"], out, ws)
+    with torch.cuda.stream(stream):
+        call()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        call()
+    torch.cuda.synchronize()
+    q0 = d["q"].clone()
+    for rep in range(3):
+        # new query values in place (same address), then the eager reference
+        d["q"].copy_(q0 if rep == 0 else torch.roll(q0, shifts=rep, dims=0))
+        out.fill_(-5)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        replayed = out.clone()
+        out.fill_(-5)
+        call()
+        torch.cuda.synchronize()
+        assert torch.equal(replayed, out), rep
+    pb.q = d["q"].cpu()
+    ref, sc = reference(pb)
+    check_prefill(pb, out, ref, sc)
 
 
 def sample_rows(pb, per_request=6, seed=4400):
