@@ -137,11 +137,16 @@ int32_t prep_score(const msa_tensor *q_idx, const msa_tensor *index_k, const msa
     const int64_t R = block_table->shape[0], MB = block_table->shape[1];
     const int64_t N = R * (int64_t)tokens_per_row;
     Di = (int)q_idx->shape[1];
-    if (q_idx->shape[0] != N || scores->shape[0] != N || scores->shape[1] != MB) c.fail(MSA_ERR_SHAPE);
+    // [N, MB]: one row per query token; [R, MB] with T > 1: one row per
+    // request, the max over its tokens
+    const bool per_row = tokens_per_row > 1 && scores->shape[0] == R;
+    if (q_idx->shape[0] != N || (scores->shape[0] != N && !per_row) || scores->shape[1] != MB)
+        c.fail(MSA_ERR_SHAPE);
     if (index_k->shape[1] != kBlock || index_k->shape[2] != Di) c.fail(MSA_ERR_SHAPE);
     qt = etype(q_idx->dtype);
     kt = etype(index_k->dtype);
     if (!score_supported(qt, kt, Di)) c.fail(MSA_ERR_UNSUPPORTED);
+    if (per_row && !score_per_row_supported(qt, kt, Di, tokens_per_row)) c.fail(MSA_ERR_UNSUPPORTED);
     if (!fits_i32(N) || !fits_i32(index_k->shape[0])) c.fail(MSA_ERR_UNSUPPORTED);
     rows16(c, q_idx);
     rows16(c, index_k);
@@ -156,6 +161,7 @@ int32_t prep_score(const msa_tensor *q_idx, const msa_tensor *index_k, const msa
     p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB;
     p.P = (int32_t)index_k->shape[0];
     p.idx_scale = idx_scale;
+    p.per_row = per_row;
     return MSA_OK;
 }
 
@@ -208,7 +214,11 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     D = (int)q->shape[2];
     const int64_t P = k_cache->shape[0], Hkv = k_cache->shape[2];
     const int64_t K = topk_idx->shape[per_head ? 2 : 1];
-    if (q->shape[0] != N || topk_idx->shape[per_head ? 1 : 0] != N) c.fail(MSA_ERR_SHAPE);
+    // selection rows: one per query token, or (T > 1) one per request shared
+    // by its tokens
+    const int64_t trows = topk_idx->shape[per_head ? 1 : 0];
+    const bool sel_per_row = tokens_per_row > 1 && trows == R;
+    if (q->shape[0] != N || (trows != N && !sel_per_row)) c.fail(MSA_ERR_SHAPE);
     if (per_head && topk_idx->shape[0] != Hkv) c.fail(MSA_ERR_SHAPE);
     if (k_cache->shape[1] != kBlock || k_cache->shape[3] != D) c.fail(MSA_ERR_SHAPE);
     for (int i = 0; i < 4; ++i)
@@ -238,6 +248,7 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     p.tk_sg = per_head ? topk_idx->stride[0] : 0;
     p.tk_sn = topk_idx->stride[per_head ? 1 : 0];
     p.tk_si = topk_idx->stride[per_head ? 2 : 1];
+    p.sel_per_row = sel_per_row;
     p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
     p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
     plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kvt);
@@ -442,7 +453,8 @@ void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *t
     if (e == MSA_OK)
         e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row, out, sm_scale,
                       k_scale, v_scale, block_size, at, plan, qt, kvt, D);
-    if (e == MSA_OK && (scores->shape[0] != (int64_t)at.R * at.T || scores->shape[1] != at.MB))
+    if (e == MSA_OK && (scores->shape[0] != (at.sel_per_row ? (int64_t)at.R : (int64_t)at.R * at.T) ||
+                        scores->shape[1] != at.MB))
         e = MSA_ERR_SHAPE;
     if (e != MSA_OK) { set_error(e); return; }
     const int32_t N = at.R * at.T;
@@ -477,6 +489,7 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
         e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row, out, sm_scale,
                       k_scale, v_scale, block_size, at, plan, qt, kvt, D);
     if (e == MSA_OK && k_cache->shape[0] != index_k->shape[0]) e = MSA_ERR_SHAPE;
+    if (e == MSA_OK && (bool)sc.per_row != (bool)at.sel_per_row) e = MSA_ERR_SHAPE;
     if (e != MSA_OK) { set_error(e); return; }
     const int32_t N = sc.R * sc.T;
     if (N == 0) return;

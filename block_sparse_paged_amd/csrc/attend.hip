@@ -75,7 +75,8 @@ __device__ int build_union(const AttnParams &p, const Group &q, uint32_t (*sel)[
     const int64_t n0 = (int64_t)q.r * p.T + q.t0;
     for (int e = tid; e < q.nt * p.k; e += 256) {
         const int t = e / p.k, i = e - t * p.k;
-        const int j = p.topk[(int64_t)q.g * p.tk_sg + (n0 + t) * p.tk_sn + (int64_t)i * p.tk_si];
+        const int64_t row = p.sel_per_row ? (int64_t)q.r : n0 + t;
+        const int j = p.topk[(int64_t)q.g * p.tk_sg + row * p.tk_sn + (int64_t)i * p.tk_si];
         if (j < 0 || j >= p.MB || j * kBlock >= token_vis(p, q, t)) continue;
         const int pid = p.bt[(int64_t)q.r * p.bt_sr + (int64_t)j * p.bt_sj];
         if (pid < 0 || pid >= p.P) continue;

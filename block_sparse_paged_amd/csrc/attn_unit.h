@@ -185,14 +185,15 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     // One round trip for the small inputs: seq_len, the selection row up to e1
     // (lane l holds entries l + 64c) or the score row, the row's block table
     // (lane l holds logical blocks l and l + 64) and the query fragments.
-    const int64_t trow = (int64_t)g * p.tk_sg + (int64_t)n * p.tk_sn;
+    const int64_t srow_n = p.sel_per_row ? r : n;   // the selection / score row
+    const int64_t trow = (int64_t)g * p.tk_sg + srow_n * p.tk_sn;
     int tkv[4];
     float srow[2];
     if constexpr (SEL) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
             const int jj = lane + 64 * c;
-            srow[c] = jj < p.MB ? p.scores[(int64_t)n * p.sc_sn + (int64_t)jj * p.sc_sj] : 0.f;
+            srow[c] = jj < p.MB ? p.scores[srow_n * p.sc_sn + (int64_t)jj * p.sc_sj] : 0.f;
         }
     } else {
 #pragma unroll
@@ -530,7 +531,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     };
     auto store_topk = [&]() {
         if constexpr (SEL) {
-            if (qs == 0 && g == 0 && wave == 0)
+            if (qs == 0 && g == 0 && wave == 0 && (!p.sel_per_row || t == 0))
                 for (int i = lane; i < p.k; i += 64) p.topk_out[trow + (int64_t)i * p.tk_si] = sslots[i];
         }
     };

@@ -19,9 +19,10 @@ struct ScoreParams {
     const void *index_k; int64_t k_sp, k_sb;       // [P, B, Di], inner stride 1
     const int32_t *bt;   int64_t bt_sr, bt_sj;     // [R, MB]
     const int32_t *seq_lens; int64_t sl_s;         // [R]
-    float *scores;       int64_t sc_sn, sc_sj;     // [N, MB]
+    float *scores;       int64_t sc_sn, sc_sj;     // [N, MB], or [R, MB] when per_row
     int32_t R, T, MB, P;
     float idx_scale;
+    int32_t per_row;                               // one sheet row per request: max over its tokens
 };
 
 struct TopkParams {
@@ -37,6 +38,7 @@ struct AttnParams {
     const int32_t *bt;   int64_t bt_sr, bt_sj;
     const int32_t *seq_lens; int64_t sl_s;
     const int32_t *topk; int64_t tk_sg, tk_sn, tk_si;  // [Hkv, N, k]; tk_sg = 0: [N, k] shared
+    int32_t sel_per_row;                           // selection (and score) rows per request: [.., R, k]
     // selection computed in the attention kernel: score sheet in, topk out
     const float *scores; int64_t sc_sn, sc_sj;     // [N, MB]
     int32_t *topk_out;                             // same strides as topk
@@ -140,6 +142,8 @@ hipError_t launch_attention(const AttnParams &p, int q_type, int kv_type, int D,
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s);
 
 bool score_supported(int q_type, int k_type, int Di);
+// a sheet row per request (the max over its T tokens) is served for decode rows
+bool score_per_row_supported(int q_type, int k_type, int Di, int T);
 bool attention_supported(int q_type, int kv_type, int D, int G);
 bool attention_uses_mfma(int q_type, int kv_type, int G);
 

@@ -173,7 +173,15 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
             for (int t = 0; t < TQ; ++t) best[t] = max_across_groups<LPT>(best[t]);
         }
     }
-    if (lane < nt) {
+    if (p.per_row) {
+        // one row per request (T <= kTokGroup: this wave holds all its
+        // tokens): the max over them (tokens past nt hold -inf)
+        float v = best[0];
+#pragma unroll
+        for (int t = 1; t < TQ; ++t) v = fmaxf(v, best[t]);
+        v = bad_page ? __builtin_nanf("") : v * p.idx_scale;
+        if (lane == 0) p.scores[(int64_t)r * p.sc_sn + (int64_t)j * p.sc_sj] = v;
+    } else if (lane < nt) {
         float v = best[0];
 #pragma unroll
         for (int t = 1; t < TQ; ++t) v = (lane == t) ? best[t] : v;
@@ -328,6 +336,13 @@ hipError_t launch_valu_di(const ScoreParams &p, int Di, hipStream_t s) {
 bool score_supported(int q_type, int k_type, int Di) {
     return (q_type == E_F32 || q_type == E_BF16) && (k_type == E_F32 || k_type == E_FP8) &&
            (Di == 32 || Di == 64 || Di == 128);
+}
+
+bool score_per_row_supported(int q_type, int k_type, int Di, int T) {
+    // the MFMA decode kernel holds a row's T <= 16 tokens in one wave; the
+    // vector kernel holds kTokGroup of them
+    const bool mfma = q_type == E_BF16 && k_type == E_FP8 && (Di == 64 || Di == 128);
+    return T <= (mfma ? 16 : kTokGroup);
 }
 
 hipError_t launch_score(const ScoreParams &p, int q_type, int k_type, int Di, hipStream_t s) {

@@ -88,7 +88,15 @@ __device__ __forceinline__ void score_page(const ScoreParams &p, const int r, co
             best = max_across_groups<16>(best);
         }
     }
-    if (grp == 0 && tok) {
+    if (p.per_row) {
+        // one row per request: the max over the row's tokens (columns past
+        // T hold -inf)
+        best = group_max<16>(best);
+        if (lane == 0) {
+            const float v = bad_page ? __builtin_nanf("") : best * p.idx_scale;
+            p.scores[(int64_t)r * p.sc_sn + (int64_t)j * p.sc_sj] = v;
+        }
+    } else if (grp == 0 && tok) {
         const float v = bad_page ? __builtin_nanf("") : best * p.idx_scale;
         p.scores[(n0 + li) * p.sc_sn + (int64_t)j * p.sc_sj] = v;
     }

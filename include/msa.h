@@ -91,7 +91,11 @@ typedef enum msa_status {
  *   tokens_per_row  T >= 1, N = R*T
  *   block_size  must be 128
  *   idx_scale   > 0, finite (static per-tensor dequantisation scale)
- *   scores      [N, MB]     f32 OUT         any strides
+ *   scores      [N, MB]     f32 OUT         any strides; or, with T > 1, [R, MB]:
+ *               one row per request (the sheet's per-request form in the
+ *               page), scores[r][j] = the max of scores[n][j] over the row's
+ *               tokens n; served for rows of up to 16 tokens on the MFMA path
+ *               and up to 4 on the vector path
  * Di must be 32, 64 or 128.  A visible block whose physical page id lies
  * outside [0, P) scores NaN (the page is not read).  With bf16 queries, an FP8
  * index and Di in {64, 128} the dot products run on bf16 MFMA tiles (one page
@@ -151,7 +155,9 @@ size_t msa_sparse_decode_workspace_bytes(int32_t rows, int32_t tokens_per_row,
  *   topk_idx    [N, k] i32, shared by all KV heads, or [Hkv, N, k] i32, one
  *               selection per KV head (attention.decode's (Hkv, B, K) layout:
  *               query head h attends the blocks of topk_idx[h / (Hq/Hkv)]);
- *               any strides
+ *               any strides.  With T > 1 the rows may also be per request
+ *               ([R, k] or [Hkv, R, k]): token r*T + t attends row r's blocks,
+ *               each token with its own visibility
  *   tokens_per_row  T >= 1
  *   out         [N, Hq, D]      bf16 | f32 OUT  any strides
  *   sm_scale, k_scale, v_scale  finite floats
@@ -184,8 +190,10 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
  * with the same wave-level radix select as msa_select_topk, and one of them
  * stores topk_idx; otherwise the top-k kernel runs first.
  *
- *   scores      [N, MB] f32, N = R * tokens_per_row, MB = block_table's width
- *   topk_idx    [N, k] i32 OUT (one selection for all KV heads: one index head)
+ *   scores      [N, MB] f32, N = R * tokens_per_row, MB = block_table's width,
+ *               or [R, MB] (per request, T > 1)
+ *   topk_idx    [N, k] i32 OUT (one selection for all KV heads: one index head),
+ *               or [R, k] with a per-request sheet: one selection per request
  *   workspace   as for msa_sparse_decode (same size query, same contract)
  */
 void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *topk_idx,
@@ -210,6 +218,8 @@ size_t msa_decode_step_workspace_bytes(int32_t rows, int32_t tokens_per_row,
  * out are all written).
  *
  *   index_k and k_cache/v_cache must have the same pool size P.
+ *   scores and topk_idx are both per token ([N, ..]) or both per request
+ *   ([R, ..], T > 1: one selection shared by the request's tokens).
  *   workspace   at least msa_decode_step_workspace_bytes(...) bytes, 256-byte
  *               aligned, zero-filled once before first use; every call leaves
  *               its counters at zero again.  Calls sharing a workspace must

@@ -140,6 +140,18 @@ def block_score(q_idx, index_k, block_table, seq_lens, T: int, idx_scale: float,
     return out
 
 
+def block_score_per_row(q_idx, index_k, block_table, seq_lens, T: int, idx_scale: float,
+                        threads: int = 1) -> np.ndarray:
+    """scores [R, MB] float64: one sheet row per request (attention.msa_block_score's
+    per-request block-max sheet in Cacheon "Kernel ABI", "Attention block slots"),
+    the block max taken over the request's T tokens as well: row r, block j holds
+    the max over the row's tokens of their block-j scores (-inf where no token sees
+    a key of block j; NaN propagates)."""
+    per_token = block_score(q_idx, index_k, block_table, seq_lens, T, idx_scale, threads=threads)
+    R = per_token.shape[0] // T
+    return per_token.reshape(R, T, -1).max(axis=1)
+
+
 def select_topk(scores, k: int) -> np.ndarray:
     """topk_idx [N, k] int32 from a score sheet (float64 or float32 values)."""
     lib = _load()
@@ -155,12 +167,19 @@ def sparse_decode(q, k_cache, v_cache, block_table, seq_lens, topk_idx, T: int,
                   n_range: Optional[tuple[int, int]] = None, threads: int = 1) -> np.ndarray:
     """out [N, Hq, D] float64 (rows outside ``n_range`` are NaN).
 
-    ``topk_idx`` is [N, K] (one selection shared by every KV head) or [Hkv, N, K]
+    ``topk_idx`` rows are per query token (N = R*T of them) or, with T > 1, per
+    request (R rows, shared by the request's tokens).  It is [N, K] (one
+    selection shared by every KV head) or [Hkv, N, K]
     (one selection per KV head, the (Hkv, B, K) layout of attention.decode in
     Cacheon "Kernel ABI", "Attention block slots"): query head h attends the
     blocks of topk_idx[h // (Hq // Hkv)].  The per-head form is the shared form
     evaluated once per KV head, keeping that head's query heads."""
     tk_all = np.asarray(torch.as_tensor(topk_idx, dtype=torch.int32).cpu())
+    N = int(q.shape[0])
+    if T > 1 and tk_all.shape[-2] == N // T and N // T != N:
+        # one selection per request, shared by its T tokens (each token keeps
+        # its own visibility): token r*T + t uses row r
+        tk_all = np.repeat(tk_all, T, axis=-2)
     if tk_all.ndim == 3:
         Hkv, Hq = k_cache.shape[2], q.shape[1]
         assert tk_all.shape[0] == Hkv and Hq % Hkv == 0

@@ -546,3 +546,46 @@ def test_prefill_select_row_mask_computes_only_marked_rows(orc):
     got, sc = orc.prefill_select(*args, return_scores=True, rows=mask, threads=2)
     assert np.array_equal(got[mask], full[mask]) and np.array_equal(sc[mask], fsc[mask])
     assert (got[~mask] == -1).all() and np.isneginf(sc[~mask]).all()
+
+
+@pytest.mark.parametrize("case", small_cases(), ids=lambda c: c.name)
+def test_per_request_score_matches_brute_force(orc, case):
+    """One sheet row per request (the max over the request's tokens), against a
+    dense route that takes the max over the tokens first and over each block's
+    keys second."""
+    got = orc.block_score_per_row(case.q_idx, case.index_k, case.block_table, case.seq_lens, case.T,
+                                  case.idx_scale)
+    qi = _decode(case.q_idx)
+    ref = np.full((case.R, case.MB), -np.inf)
+    for r in range(case.R):
+        L = int(case.seq_lens[r])
+        if L == 0:
+            continue
+        K = _dense_keys(case, case.index_k, r)
+        rows = range(r * case.T, (r + 1) * case.T)
+        dots = qi[list(rows)] @ K.T
+        vis = np.array([case.visible(n) for n in rows])
+        dots = np.where(np.arange(L)[None, :] < vis[:, None], dots, -np.inf).max(axis=0)   # [L]
+        dots = np.concatenate([dots, np.full(case.MB * case.B - L, -np.inf)])
+        ref[r] = dots.reshape(case.MB, case.B).max(axis=1) * case.idx_scale
+    assert got.shape == (case.R, case.MB)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    assert np.allclose(got[fin], ref[fin], rtol=1e-12, atol=1e-12)
+
+
+def test_attention_per_request_selection(orc):
+    """A selection per request ([R, K], and [Hkv, R, K]) is attended by every
+    token of the request, each with its own visibility: the brute-force route
+    with the rows repeated per token."""
+    case = synth.make_case("per_row", R=3, T=3, Hq=4, Hkv=2, D=8, Di=4, seq_lens=[21, 9, 14], P=16,
+                           k=3, fp8=True, seed=17, B=4)
+    rng = np.random.default_rng(18)
+    rows = np.stack([rng.choice(case.MB, size=case.k, replace=False) for _ in range(case.R)]).astype(np.int32)
+    got = _attn(orc, case, rows)
+    ref = brute_attention(case, np.repeat(rows, case.T, axis=0))
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    per_head = np.stack([rows, rows[::-1].copy()])
+    got = _attn(orc, case, per_head)
+    ref = brute_attention(case, np.repeat(per_head, case.T, axis=1))
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)

@@ -8,7 +8,7 @@ import pytest
 import torch
 
 import synth
-from msa_harness import check_attention, oracle_attention, poisoned, upload, workspace
+from msa_harness import check_attention, check_scores, oracle_attention, poisoned, upload, workspace
 
 pytestmark = pytest.mark.gpu
 
@@ -145,3 +145,100 @@ def test_per_head_selection_shape_is_checked(msa):
         msa.msa_select_sparse_decode(scores, c.k, tk3, d.q, d.k_cache, d.v_cache, d.block_table,
                                      d.seq_lens, c.T, out, c.sm_scale, c.k_scale, c.v_scale, c.B,
                                      workspace(msa, c, c.k))
+
+
+# ---- one selection per request, shared by its tokens (per-request sheet)
+
+PER_ROW = [
+    # MFMA decode score + MFMA attention (bf16 queries, FP8, 16 query heads per KV head)
+    dict(R=3, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[900, 3000, 129], P=40, k=6),
+    # vector score (f32 index queries, 3 tokens) + vector attention, Di = D = 64
+    dict(R=2, T=3, Hq=8, Hkv=2, D=64, Di=64, seq_lens=[700, 1500], P=25, k=4, fp8=False),
+]
+
+
+def per_row_case(spec, seed):
+    return synth.make_case("per_row", seed=seed, **spec)
+
+
+@pytest.mark.parametrize("spec", PER_ROW, ids=["mfma", "valu"])
+def test_per_request_sheet_selection_attention(msa, spec):
+    """msa_block_score into an [R, MB] sheet (one row per request: the max
+    over its tokens), msa_select_topk over it, msa_sparse_decode with the
+    [R, k] selection shared by each request's tokens (and as [Hkv, R, k])."""
+    import oracle
+    c = per_row_case(spec, seed=71)
+    print(f"case per_row {spec}", flush=True)
+    d = upload(c)
+    scores = poisoned((c.R, c.MB), torch.float32)
+    msa.msa_block_score(d.q_idx, d.index_k, d.block_table, d.seq_lens, c.T, c.B, c.idx_scale, scores)
+    tk = poisoned((c.R, c.k), torch.int32)
+    msa.msa_select_topk(scores, c.k, tk)
+    torch.cuda.synchronize()
+    gs, gt = scores.cpu().numpy(), tk.cpu().numpy()
+    ref_s = oracle.block_score_per_row(c.q_idx, c.index_k, c.block_table, c.seq_lens, c.T,
+                                       c.idx_scale, threads=8)
+    check_scores(gs, ref_s)
+    assert np.array_equal(gt, oracle.select_topk(gs.astype(np.float64), c.k))
+    out = attend(msa, c, d, tk, out_dtype=torch.bfloat16 if c.fp8 else torch.float32)
+    check_attention(out, oracle_attention(c, gt))
+    if c.Hkv > 1:
+        tk3 = np.stack([gt, gt[::-1].copy()])
+        out = attend(msa, c, d, torch.from_numpy(tk3).cuda(),
+                     out_dtype=torch.bfloat16 if c.fp8 else torch.float32)
+        check_attention(out, oracle_attention(c, tk3))
+
+
+def test_per_request_select_and_step_calls(msa):
+    """msa_select_sparse_decode and msa_decode_step with a per-request sheet
+    and selection: the selection is the oracle's on the GPU's own sheet, and
+    the outputs equal the separate calls' bit for bit."""
+    import oracle
+    c = per_row_case(PER_ROW[0], seed=72)
+    d = upload(c)
+    ws = workspace(msa, c, c.k)
+    scores = poisoned((c.R, c.MB), torch.float32)
+    tk = poisoned((c.R, c.k), torch.int32)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_decode_step(d.q_idx, d.index_k, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                        c.T, c.k, c.B, c.idx_scale, c.sm_scale, c.k_scale, c.v_scale, scores, tk,
+                        out, ws)
+    torch.cuda.synchronize()
+    gs, gt = scores.cpu().numpy(), tk.cpu().numpy()
+    ref_s = oracle.block_score_per_row(c.q_idx, c.index_k, c.block_table, c.seq_lens, c.T,
+                                       c.idx_scale, threads=8)
+    check_scores(gs, ref_s)
+    assert np.array_equal(gt, oracle.select_topk(gs.astype(np.float64), c.k))
+    check_attention(out, oracle_attention(c, gt))
+    # the two-stage call on the same sheet, and the attention alone
+    tk2 = poisoned((c.R, c.k), torch.int32)
+    out2 = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_select_sparse_decode(scores, c.k, tk2, d.q, d.k_cache, d.v_cache, d.block_table,
+                                 d.seq_lens, c.T, out2, c.sm_scale, c.k_scale, c.v_scale, c.B, ws)
+    out3 = attend(msa, c, d, tk)
+    torch.cuda.synchronize()
+    assert torch.equal(tk2, tk)
+    assert torch.equal(out2.view(torch.int16), out.view(torch.int16))
+    assert torch.equal(out3.view(torch.int16), out.view(torch.int16))
+
+
+def test_per_request_shapes_checked(msa):
+    c = per_row_case(PER_ROW[0], seed=73)
+    d = upload(c)
+    ws = workspace(msa, c, c.k)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    # a per-request sheet with a per-token selection (and the reverse) disagree
+    with pytest.raises(msa.MsaError, match="sizes disagree"):
+        msa.msa_decode_step(d.q_idx, d.index_k, d.q, d.k_cache, d.v_cache, d.block_table,
+                            d.seq_lens, c.T, c.k, c.B, c.idx_scale, c.sm_scale, c.k_scale,
+                            c.v_scale, poisoned((c.R, c.MB), torch.float32),
+                            poisoned((c.N, c.k), torch.int32), out, ws)
+    # per-request sheets are served for decode rows (T <= 16) only
+    big = synth.make_case("per_row_prefill", R=1, T=40, Hq=16, Hkv=1, D=128, Di=128,
+                          seq_lens=[600], P=8, k=2, seed=74)
+    db = upload(big)
+    with pytest.raises(msa.MsaError, match="size outside"):
+        msa.msa_block_score(db.q_idx, db.index_k, db.block_table, db.seq_lens, big.T, big.B,
+                            big.idx_scale, poisoned((big.R, big.MB), torch.float32))
+    torch.cuda.synchronize()
+    assert torch.isnan(out.float()).all()
