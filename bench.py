@@ -340,6 +340,40 @@ def cpu_baseline(case, min_wall: float = 1.0) -> dict:
                       f"(score+select+attend, fp64 C, {threads} threads), {dt:.2f} s wall"}
 
 
+def prefill_cpu_baseline(synth, rows_per_request: int = 2) -> dict:
+    """The oracle's ragged prefill score-to-selection on a bounded sample of the
+    workload's rows (head 0, the first and the last query block of every
+    request), extrapolated to the whole call by the count of dot products."""
+    import oracle
+    pb = synth.prefill_ragged()
+    cu = pb.cu_seqblocks_q.numpy()
+    cus = pb.cu_seqlens.numpy()
+    rows = np.zeros((pb.Hq, pb.all_qb), dtype=bool)
+
+    def dots(b, qb):
+        nq = int(cus[b + 1] - cus[b])
+        ntok = min(pb.block_size_q, nq - qb * pb.block_size_q)
+        return ntok * min(int(pb.seq_lens[b]), int(pb.prefix_lens[b]) + qb * pb.block_size_q)
+    sample = total = 0
+    for b in range(pb.batch):
+        n = int(cu[b + 1] - cu[b])
+        for qb in range(n):
+            total += dots(b, qb) * pb.Hq
+        for qb in sorted({0, n - 1})[:rows_per_request]:
+            rows[0, cu[b] + qb] = True
+            sample += dots(b, qb)
+    t0 = time.perf_counter()
+    oracle.prefill_select(pb.q, pb.index_k, pb.block_table, pb.slot_ids, pb.cu_seqlens, pb.seq_lens,
+                          pb.prefix_lens, pb.block_size_q, pb.topk, pb.init_blocks, pb.local_blocks,
+                          pb.scale, pb.cu_seqblocks_q, pb.all_qb, threads=1, rows=rows)
+    dt = time.perf_counter() - t0
+    per_call = dt * total / sample
+    return {"value": round(1.0 / per_call, 6), "unit": "calls/s", "cores": 1, "kind": "oracle",
+            "sample": f"{int(rows.sum())} of {pb.Hq * pb.all_qb} (head, query-block) rows (head 0, first and "
+                      f"last query block of each request), {dt:.2f} s wall on one thread, scaled by "
+                      f"dot products ({sample} of {total}) to {per_call:.1f} s per call"}
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -495,6 +529,8 @@ def main():
     if not a.no_prefill:
         res["prefill_score"] = prefill_score(torch, msa, synth)
         res["prefill_select_ragged"] = prefill_select_ragged(torch, msa, synth)
+        if not a.no_cpu_baseline:
+            res["prefill_select_ragged"]["cpu_baseline"] = prefill_cpu_baseline(synth)
     if not a.no_variants:
         del pools, scores, out, ws
         res["bf16_kv_attention"] = bf16_kv_attention(torch, msa, case, tk_host)
