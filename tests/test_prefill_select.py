@@ -290,3 +290,34 @@ def check_format(pb, gpu):
             assert len(sel) == min(pb.topk, ncand)
             forced = [j for j in range(ncand) if j < pb.init_blocks or j >= ncand - pb.local_blocks]
             assert set(forced[:pb.topk]) <= set(sel.tolist())
+
+
+def test_prefill_select_strided_views(msa):
+    """Every tensor passed as a strided view (query heads sliced out of a wider
+    tensor, padded index pages, a transposed block table, offsets with stride 2,
+    a permuted out_topk): the same selection as the contiguous call, bit for
+    bit."""
+    pb = synth.prefill_batch("strided", new_tokens=[200, 77, 130], prefix=[1500, 300, 4000], Hq=4,
+                             Di=128, block_size_q=64, topk=5, init_blocks=1, local_blocks=1,
+                             seed=4307, extra_qb_rows=2)
+    d = upload(pb)
+    ref = run(msa, pb, d)
+    qw = torch.zeros((pb.total_q, pb.Hq + 2, pb.Di), dtype=torch.bfloat16, device="cuda")
+    qw[:, 1:pb.Hq + 1] = d["q"]
+    kw = torch.zeros((pb.P, 130, pb.Di), dtype=torch.uint8, device="cuda")
+    kw[:, :128] = d["index_k"].view(torch.uint8)
+    btw = d["block_table"].t().contiguous().t()                   # column-major
+
+    def stride2(x):
+        return torch.stack([x, torch.full_like(x, -99)], dim=1)[:, 0]
+    sv = {n: stride2(d[n]) for n in ("slot_ids", "cu_seqlens", "seq_lens", "prefix_lens",
+                                     "cu_seqblocks_q")}
+    assert all(v.stride(0) == 2 for v in sv.values())
+    outw = poisoned((pb.topk, pb.all_qb, pb.Hq), torch.int32).permute(2, 1, 0)
+    ws = prefill_workspace(msa, pb)
+    msa.msa_prefill_block_score(qw[:, 1:pb.Hq + 1], kw[:, :128].view(torch.float8_e4m3fn), btw,
+                                sv["slot_ids"], sv["cu_seqlens"], sv["seq_lens"], sv["prefix_lens"],
+                                pb.block_size_q, pb.B, pb.topk, pb.init_blocks, pb.local_blocks,
+                                pb.scale, sv["cu_seqblocks_q"], outw, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(outw, ref)
