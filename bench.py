@@ -317,6 +317,105 @@ def bf16_kv_attention(torch, msa, case, topk, copies: int = 4, reps: int = 50) -
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
+def time_sparse_decode(torch, msa, case, pools, tk, out_dtype, copies: int, reps: int) -> float:
+    """Seconds per msa_sparse_decode over `pools` [(k_cache, v_cache)] rotated in
+    a graph (cold copies), selection tensor `tk` on the device."""
+    dev = "cuda"
+    q, bt, sl = case.q.to(dev), case.block_table.to(dev), case.seq_lens.to(dev)
+    out = torch.empty((case.N, case.Hq, case.D), dtype=out_dtype, device=dev)
+    ws = torch.zeros(msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D,
+                                                           tk.shape[-1]), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.Stream()
+
+    def body():
+        for kc, vc in pools:
+            msa.msa_sparse_decode(q, kc, vc, bt, sl, tk, case.T, out, case.sm_scale, case.k_scale,
+                                  case.v_scale, case.B, ws)
+    with torch.cuda.stream(stream):
+        body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        body()
+    with torch.cuda.stream(stream):
+        for _ in range(5):
+            g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1000.0 / (reps * len(pools))
+
+
+def kv_bytes(case, sel_rows) -> int:
+    """K/V bytes of one KV head's selection: every visible token of the union of
+    the selected blocks of each row, K and V, D bytes each (FP8)."""
+    lens = case.seq_lens.numpy().astype(np.int64)
+    tokens = 0
+    for r in range(case.R):
+        ids = np.unique(sel_rows[r])
+        ids = ids[ids >= 0]
+        tokens += int(sum(min(case.B, lens[r] - j * case.B) for j in ids if j * case.B < lens[r]))
+    return tokens * case.D * 2
+
+
+def per_request_selection(torch, msa, case, copies: int = 4, reps: int = 50) -> dict:
+    """msa_sparse_decode with one selection per request ([R, k], shared by the
+    request's 4 tokens), made on the device from the per-request score sheet
+    (msa_block_score into [R, MB] + msa_select_topk), on cold pool copies."""
+    dev = "cuda"
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    sheet = torch.empty((case.R, case.MB), device=dev)
+    msa.msa_block_score(case.q_idx.to(dev), f8(case.index_k).to(dev), case.block_table.to(dev),
+                        case.seq_lens.to(dev), case.T, case.B, case.idx_scale, sheet)
+    tk = torch.empty((case.R, case.k), dtype=torch.int32, device=dev)
+    msa.msa_select_topk(sheet, case.k, tk)
+    k0, v0 = f8(case.k_cache).to(dev), f8(case.v_cache).to(dev)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    t = time_sparse_decode(torch, msa, case, pools, tk, torch.bfloat16, copies, reps)
+    tkh = tk.cpu().numpy()
+    nbytes = (kv_bytes(case, tkh) * case.Hkv + case.N * case.Hq * case.D * 2 * 2 + case.R * case.k * 4
+              + case.R * case.MB * 4 + case.R * 4)
+    gbs = nbytes / t / 1e9
+    return {"workload": "msa_sparse_decode, 16 rows x 4 tokens, 16384 ctx, top-k 16, one selection per "
+                        "request ([16, 16], from the per-request sheet)",
+            "us": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "kernel": "attn_token_kernel<128, 2>", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def per_kv_head_selection(torch, msa, synth, case, copies: int = 4, reps: int = 50) -> dict:
+    """msa_sparse_decode with 32 query / 2 KV heads and one selection per KV
+    head ([2, 64, 16], random visible blocks), 16 rows x 4 tokens at 16384
+    context, on cold pool copies.  The second KV head's pages are the bench
+    pool's pages shifted by one page, and its 16 query heads the bench queries
+    shifted by one token (built on the device)."""
+    import dataclasses
+    dev = "cuda"
+    u8 = lambda t: t.view(torch.uint8).to(dev)
+    two = lambda t: torch.stack([t[:, :, 0], t.roll(1, dims=0)[:, :, 0]], dim=2).view(torch.float8_e4m3fn)
+    k0, v0 = two(u8(case.k_cache)), two(u8(case.v_cache))
+    c2 = dataclasses.replace(case, name="hbm_hkv2", Hq=32, Hkv=2,
+                             q=torch.cat([case.q, case.q.roll(1, dims=0)], dim=1))
+    tkh = np.stack([synth.random_topk(c2, seed=5101 + g).numpy() for g in range(c2.Hkv)])
+    tk = torch.from_numpy(tkh).to(dev)
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(copies - 1)]
+    t = time_sparse_decode(torch, msa, c2, pools, tk, torch.bfloat16, copies, reps)
+    rows = lambda g: [tkh[g][r * c2.T:(r + 1) * c2.T] for r in range(c2.R)]
+    nbytes = (sum(kv_bytes(c2, rows(g)) for g in range(c2.Hkv)) + c2.N * c2.Hq * c2.D * 2 * 2
+              + tkh.size * 4 + c2.R * c2.MB * 4 + c2.R * 4)
+    gbs = nbytes / t / 1e9
+    return {"workload": "msa_sparse_decode, 16 rows x 4 tokens, 16384 ctx, 32 q / 2 KV heads, top-k 16 "
+                        "per KV head ([2, 64, 16], random visible blocks)",
+            "us": round(t * 1e6, 3), "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "kernel": "attn_token_kernel<128, 2>", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
 def cpu_baseline(case, min_wall: float = 1.0) -> dict:
     """The oracle's full step on the host cores, repeated for at least min_wall s."""
     import oracle
@@ -534,6 +633,8 @@ def main():
     if not a.no_variants:
         del pools, scores, out, ws
         res["bf16_kv_attention"] = bf16_kv_attention(torch, msa, case, tk_host)
+        res["per_request_selection"] = per_request_selection(torch, msa, case)
+        res["per_kv_head_selection"] = per_kv_head_selection(torch, msa, synth, case)
     if a.calib_copy_mib > 0:
         # the reference copy's size and the calls' algorithmic bytes, for --pmc-summary
         os.makedirs(a.calib_out, exist_ok=True)
