@@ -339,7 +339,7 @@ int32_t prep_prefill(const msa_tensor *q, const msa_tensor *index_k, const msa_t
         c.fail(MSA_ERR_UNSUPPORTED);
     if (!c.ok()) return c.err;
     const PrefillGeom g = prefill_geom(batch, Hq, all_qb, MB, block_size_q);
-    if (g.Pmax > 0x7fffffff) c.fail(MSA_ERR_UNSUPPORTED);   // pages are counted in int
+    if (g.Wmax > 0x7fffffff) c.fail(MSA_ERR_UNSUPPORTED);   // share weights are counted in int
     rows16(c, q);
     rows16(c, index_k);
     if (!c.ok()) return c.err;

@@ -76,7 +76,7 @@ struct PrefillGeom {
     int32_t NP;     // parts per query block (1 unless bsq > kPrefillCols)
     int32_t HG;     // head groups: ceil(Hq / hc)
     int64_t Cmax;   // chunks at most
-    int64_t Pmax;   // pages (chunk x visible block) at most
+    int64_t Wmax;   // share weight at most: every chunk's pages plus its ramp weight
 };
 
 struct PrefillSelParams {

@@ -488,7 +488,7 @@ PrefillGeom prefill_geom(int64_t batch, int64_t Hq, int64_t all_qb, int64_t MB, 
     }
     g.HG = (int32_t)((Hq + g.hc - 1) / g.hc);
     g.Cmax = ((all_qb + g.nqc - 1) / g.nqc + batch) * g.HG * g.NP;
-    g.Pmax = g.Cmax * MB;
+    g.Wmax = g.Cmax * (MB + kRampWeight);
     return g;
 }
 
