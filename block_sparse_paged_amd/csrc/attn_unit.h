@@ -17,14 +17,7 @@ constexpr int kChunk = 32;                 // keys per LDS sub-chunk
 constexpr int kAttnWaves = 8;              // waves per attention workgroup
 constexpr int kWaveKeys = 64;              // keys of a page one wave takes
 constexpr int kWaveChunks = kWaveKeys / kChunk;   // 2
-#ifndef MSA_ATTN_PIPE_KEYS
-#define MSA_ATTN_PIPE_KEYS 32
-#endif
-#ifndef MSA_ATTN_KFIRST
-#define MSA_ATTN_KFIRST 0
-#endif
-constexpr int kPipeKeys = MSA_ATTN_PIPE_KEYS;   // keys per pipeline chunk (32 or 64)
-constexpr bool kKFirst = MSA_ATTN_KFIRST;       // issue all K rows before the V rows
+constexpr int kPipeKeys = 32;              // keys per pipeline chunk (one softmax update)
 
 //
 // One workgroup of 8 waves per (query token n, KV head g, split s of n's
@@ -289,7 +282,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         // function of the lane alone (KPL is a multiple of 8); V units by
         // vswz(key), which also depends on l (bit 4 of the key) but not on the
         // sub-chunk.  Order: per pipeline chunk, its K sub-chunks then its V
-        // sub-chunks (kKFirst: all K, then all V).
+        // sub-chunks.
         {
             const int key0 = lane / CPR, slot = lane % CPR;
             const uint8_t *ka = kp + (int64_t)key0 * ksb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
@@ -313,19 +306,12 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                     dma16_nt(vp + (int64_t)(sc * CHK + key) * vsb + ((slot ^ sw) << 4), vc[sc] + l * 1024);
                 }
             };
-            if constexpr (kKFirst) {
 #pragma unroll
-                for (int sc = 0; sc < kWaveChunks; ++sc) issue_k(sc);
+            for (int c = 0; c < NC; ++c) {
 #pragma unroll
-                for (int sc = 0; sc < kWaveChunks; ++sc) issue_v(sc);
-            } else {
+                for (int u = 0; u < NS; ++u) issue_k(c * NS + u);
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
-#pragma unroll
-                    for (int u = 0; u < NS; ++u) issue_k(c * NS + u);
-#pragma unroll
-                    for (int u = 0; u < NS; ++u) issue_v(c * NS + u);
-                }
+                for (int u = 0; u < NS; ++u) issue_v(c * NS + u);
             }
         }
         const bool full = kbase + WK <= vis;           // every key visible to this token
@@ -338,8 +324,8 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
             constexpr int c = decltype(C)::value;
             // loads issued after the last K (V) load of chunk c
             constexpr int CL = NS * LPC;               // loads per chunk per tensor
-            constexpr int after_k = kKFirst ? CL * (NC - 1 - c) + NC * CL : CL + 2 * CL * (NC - 1 - c);
-            constexpr int after_v = kKFirst ? CL * (NC - 1 - c) : 2 * CL * (NC - 1 - c);
+            constexpr int after_k = CL + 2 * CL * (NC - 1 - c);
+            constexpr int after_v = 2 * CL * (NC - 1 - c);
             // ---- K rows of chunk c landed
             wait_vmcnt<after_k>();
             // S^T tiles: sacc[u][e] = q . k for key c*CK + 16*u + 4*grp + e and
