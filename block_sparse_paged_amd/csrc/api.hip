@@ -361,16 +361,16 @@ int32_t prep_prefill(const msa_tensor *q, const msa_tensor *index_k, const msa_t
     return MSA_OK;
 }
 
-// workgroups of the persistent prefill scoring launch: the current device's
-// CUs, a multiple of the 8 XCDs
+// workgroups of the persistent prefill scoring launch: kPrefillWGsPerCU per
+// CU of the current device, a multiple of the 8 XCDs
 int32_t prefill_workgroups() {
     static int cache[64] = {0};
     int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256 * kPrefillWGsPerCU;
     if (!cache[dev]) {
         int n = 0;
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 8) n = 256;
-        cache[dev] = n / 8 * 8;
+        cache[dev] = n / 8 * 8 * kPrefillWGsPerCU;
     }
     return cache[dev];
 }

@@ -67,7 +67,9 @@ struct ReduceParams {
 // query blocks of a group of heads (bsq <= kPrefillCols), or a part of one
 // query block of one head; the scoring workgroups share the chunks' visible
 // blocks ("pages") evenly, in tiles of at most kPMaxPC blocks of one chunk.
-constexpr int kPrefillCols = 512;            // columns of a chunk (one 8-wave tile of 4 MFMA column tiles)
+constexpr int kPrefillWaves = 8;             // waves per scoring workgroup (two per SIMD)
+constexpr int kPrefillWGsPerCU = 1;          // scoring workgroups resident per CU
+constexpr int kPrefillCols = 16 * 4 * kPrefillWaves;   // columns of a chunk: 4 MFMA column tiles per wave
 constexpr int kPlanMaxBatch = 8192;          // requests one call takes
 
 struct PrefillGeom {

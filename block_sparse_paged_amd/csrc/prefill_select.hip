@@ -162,15 +162,19 @@ __device__ __forceinline__ void fill_rows_none(const PrefillSelParams &p, int g,
 constexpr int kRaggedPC = 14;
 // requests whose fields the prologue keeps in LDS (larger batches re-read them)
 constexpr int kLdsReqs = 512;
+// page buffers of a scoring workgroup: two groups of two pages, one barrier
+// per pair (two 4-wave workgroups per CU with one page per barrier and
+// 256-column chunks were measured slower: every page is staged per chunk)
+constexpr int kRaggedBufs = 4;
 // the fixed cost of a tile (queries and first pages on their way), in pages
 constexpr int kRampWeight = 3;
 
 template <int DI>
-__global__ __launch_bounds__(64 * kPWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(64 * kPrefillWaves) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_score_ragged_kernel(PrefillSelParams p) {
-    constexpr int QT = kPrefillCols / (16 * kPWaves);
-    constexpr int NT = 64 * kPWaves;
-    using Lds = PrefillLds<DI, QT, kRaggedPC>;
+    constexpr int QT = kPrefillCols / (16 * kPrefillWaves);
+    constexpr int NT = 64 * kPrefillWaves;
+    using Lds = PrefillLds<DI, QT, kRaggedPC, kPrefillWaves, kRaggedBufs>;
     static_assert(Lds::PQ == kPrefillCols, "chunk columns = tile columns");
     static_assert(sizeof(Lds::kb) >= 4 * (kPlanMaxBatch + 4 + 8 * kLdsReqs), "prologue tables in the page buffers");
     __shared__ Lds lds;
@@ -344,7 +348,7 @@ void prefill_score_ragged_kernel(PrefillSelParams p) {
         const int qb0 = gqc * g.nqc, nqbg = min(gr.nqb, qb0 + g.nqc) - qb0;
         const int nh = min(p.Hq, gh0 + hc) - gh0;
         int *hist = (int *)&lds.kb[0][0] + 256 * wave;   // the page buffers are idle here
-        for (int i = wave; i < nqbg * nh; i += kPWaves) {
+        for (int i = wave; i < nqbg * nh; i += kPrefillWaves) {
             const int ql = i / nh, h = gh0 + (i - ql * nh);
             if (grow0 + ql < p.all_qb) select_prefill_row<2>(p, gr, h, grow0 + ql, qb0 + ql, hist);
         }
@@ -507,7 +511,7 @@ void prefill_carve_workspace(void *ws, int64_t batch, int64_t Hq, int64_t all_qb
     p.g = prefill_geom(batch, Hq, all_qb, MB, bsq);
     // selection inside the scoring launch when a group's rows fit a few
     // selections per wave and a score row fits two keys per lane
-    p.fused = MB <= 128 && (int64_t)p.g.nqc * p.g.hc <= 4 * kPWaves;
+    p.fused = MB <= 128 && (int64_t)p.g.nqc * p.g.hc <= 4 * kPrefillWaves;
     uint8_t *b = (uint8_t *)ws;
     p.counters = (int32_t *)b;
     b += align256(4 * (size_t)(Hq * all_qb));
@@ -519,9 +523,9 @@ void prefill_carve_workspace(void *ws, int64_t batch, int64_t Hq, int64_t all_qb
 hipError_t launch_prefill_select(const PrefillSelParams &p, int Di, hipStream_t s) {
     if ((int64_t)p.Hq * p.all_qb == 0) return hipSuccess;
     if (Di == 128)
-        hipLaunchKernelGGL(prefill_score_ragged_kernel<128>, dim3(p.nwg), dim3(64 * kPWaves), 0, s, p);
+        hipLaunchKernelGGL(prefill_score_ragged_kernel<128>, dim3(p.nwg), dim3(64 * kPrefillWaves), 0, s, p);
     else
-        hipLaunchKernelGGL(prefill_score_ragged_kernel<64>, dim3(p.nwg), dim3(64 * kPWaves), 0, s, p);
+        hipLaunchKernelGGL(prefill_score_ragged_kernel<64>, dim3(p.nwg), dim3(64 * kPrefillWaves), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.fused) return e;
     if (p.MB <= 64) return launch_select<1>(p, s);

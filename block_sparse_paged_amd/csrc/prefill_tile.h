@@ -64,13 +64,14 @@ __device__ __forceinline__ void prefill_mma(const uint4 (&a)[DI / 32], const uin
                 __builtin_bit_cast(bf16x8, a[ks]), __builtin_bit_cast(bf16x8, qf[qt][ks]), acc[qt], 0, 0, 0);
 }
 
-// LDS of one tile of at most MPC blocks: two pairs of bf16 page buffers and
-// the block maxima.
-template <int DI, int QT, int MPC>
+// LDS of one tile of at most MPC blocks, worked by NW waves: NB bf16 page
+// buffers (two groups of NB/2 pages) and the block maxima.
+template <int DI, int QT, int MPC, int NW = kPWaves, int NB = 4>
 struct PrefillLds {
-    static constexpr int PQ = 16 * QT * kPWaves;    // query columns
+    static constexpr int PQ = 16 * QT * NW;         // query columns
     static constexpr int MaxPages = MPC;
-    __attribute__((aligned(16))) uint8_t kb[4][kBlock * DI * 2];
+    static constexpr int Waves = NW;
+    __attribute__((aligned(16))) uint8_t kb[NB][kBlock * DI * 2];
     float sbuf[PQ][MPC + 1];
 };
 
@@ -94,20 +95,22 @@ struct PrefillPages {
 // query row (any valid address for columns that are not used), vis(col) the
 // number of keys the column sees (0 for unused columns).  Every thread of the
 // workgroup calls it; it ends with a barrier, after which sbuf is complete.
-template <int DI, int QT, int MPC, class QRow, class Vis>
+template <int DI, int QT, int MPC, int NW, int NB, class QRow, class Vis>
 __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, Vis vis,
-                                             PrefillLds<DI, QT, MPC> &lds) {
+                                             PrefillLds<DI, QT, MPC, NW, NB> &lds) {
     constexpr int KS = DI / 32;                 // MFMA k-steps per 16-key tile
-    constexpr int NT = 64 * kPWaves;            // threads per workgroup
+    constexpr int NT = 64 * NW;                 // threads per workgroup
+    constexpr int G = NB / 2;                   // pages per group (one barrier per group)
     constexpr int RB = DI * 2;                  // bytes per bf16 row (query or key)
     constexpr int UPR = DI / 8;                 // 16-byte units per bf16 row
     constexpr int VPT = kBlock * DI / (16 * NT) > 0 ? kBlock * DI / (16 * NT) : 1;  // 16-byte FP8 loads per slice
     constexpr int TPK = DI / (16 * VPT);        // slices per key row
     constexpr int NLD = TPK * kBlock;           // threads holding a slice (whole waves)
-    constexpr int PQ = PrefillLds<DI, QT, MPC>::PQ;
+    constexpr int PQ = PrefillLds<DI, QT, MPC, NW, NB>::PQ;
     static_assert(MPC < 64, "page ids live one per lane");
+    static_assert(NB == 2 || NB == 4, "one or two pages per group");
     static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
-    static_assert(kPWaves * 16 * RB <= 2 * kBlock * RB, "query transpose area inside the first pair");
+    static_assert(NW * 16 * RB <= G * kBlock * RB, "query transpose area inside the first group");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -128,7 +131,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
     // this thread's slice of a page (threads below NLD): key tid / TPK, bytes
     // 16*VPT*(tid % TPK) ..
     const int skey = tid / TPK, spart = tid % TPK;
-    uint4 pv[2][VPT];                                      // the slices of the next pair of pages
+    uint4 pv[G][VPT];                                      // the slices of the next group of pages
     auto load_page = [&](int pi, uint4 (&v)[VPT]) {
         if (NLD < NT && tid >= NLD) return;
         const int pid = __builtin_amdgcn_readlane(pid_l, pi);
@@ -151,12 +154,15 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
             *(uint4 *)(row + (((u0 + 1) ^ (skey & (UPR - 1))) << 4)) = hi;
         }
     };
-    // Pages go through LDS two at a time (one barrier per pair).  The first
-    // pair is requested before the query rows: the other order was measured
-    // to be far slower.
-    int c0 = next_live(), c1 = next_live();
-    if (c0 >= 0) load_page(c0, pv[0]);
-    if (c1 >= 0) load_page(c1, pv[1]);
+    // Pages go through LDS G at a time (one barrier per group).  The first
+    // group is requested before the query rows: the other order was measured
+    // to be slower.
+    int cur[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        cur[u] = next_live();
+        if (cur[u] >= 0) load_page(cur[u], pv[u]);
+    }
 
     // Query rows, read coalesced.  In the MFMA operand layout consecutive
     // lanes hold different query rows, and a global load in that layout
@@ -213,19 +219,23 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
         }
     }
 
-    // first pair to LDS (once every wave is done with its transpose area);
-    // the next pair's slices on their way
+    // first group to LDS (once every wave is done with its transpose area);
+    // the next group's slices on their way
     __syncthreads();
-    if (c0 >= 0) store_page(pv[0], lds.kb[0]);
-    if (c1 >= 0) store_page(pv[1], lds.kb[1]);
-    int n0 = next_live(), n1 = next_live();
-    if (n0 >= 0) load_page(n0, pv[0]);
-    if (n1 >= 0) load_page(n1, pv[1]);
+    int nxt[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+        if (cur[u] >= 0) store_page(pv[u], lds.kb[u]);
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        nxt[u] = next_live();
+        if (nxt[u] >= 0) load_page(nxt[u], pv[u]);
+    }
     __syncthreads();
 
     const float scale = pg.scale;
-    auto compute_page = [&](const uint8_t *buf, int cur) {
-        const int kbase = (j0 + cur) * kBlock;
+    auto compute_page = [&](const uint8_t *buf, int pidx) {
+        const int kbase = (j0 + pidx) * kBlock;
         float best[QT];
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) best[qt] = -INFINITY;
@@ -271,24 +281,32 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
 #pragma unroll
         for (int qt = 0; qt < QT; ++qt) {
             const float v = max_across_groups<16>(best[qt]);
-            if (grp == 0) lds.sbuf[16 * QT * wave + 16 * qt + li][cur] = v * scale;
+            if (grp == 0) lds.sbuf[16 * QT * wave + 16 * qt + li][pidx] = v * scale;
         }
     };
-    for (int i = 0; c0 >= 0; ++i) {
-        const int b = 2 * (i & 1);
-        compute_page(lds.kb[b], c0);
-        if (c1 >= 0) compute_page(lds.kb[b + 1], c1);
-        // the other pair of buffers held the previous pair, done by every
+    for (int i = 0; cur[0] >= 0; ++i) {
+        const int b = G * (i & 1);
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            if (cur[u] >= 0) compute_page(lds.kb[b + u], cur[u]);
+        // the other group of buffers held the previous group, done by every
         // wave before the last barrier
-        const int nb = 2 - b;
-        if (n0 >= 0) store_page(pv[0], lds.kb[nb]);
-        if (n1 >= 0) store_page(pv[1], lds.kb[nb + 1]);
-        const int a0 = next_live(), a1 = next_live();
-        if (a0 >= 0) load_page(a0, pv[0]);
-        if (a1 >= 0) load_page(a1, pv[1]);
+        const int nb = G - b;
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+            if (nxt[u] >= 0) store_page(pv[u], lds.kb[nb + u]);
+        int aft[G];
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            aft[u] = next_live();
+            if (aft[u] >= 0) load_page(aft[u], pv[u]);
+        }
         __syncthreads();
-        c0 = n0; c1 = n1;
-        n0 = a0; n1 = a1;
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            cur[u] = nxt[u];
+            nxt[u] = aft[u];
+        }
     }
 }
 
