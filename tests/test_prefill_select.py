@@ -321,3 +321,29 @@ def test_prefill_select_strided_views(msa):
                                 pb.scale, sv["cu_seqblocks_q"], outw, ws)
     torch.cuda.synchronize()
     assert torch.equal(outw, ref)
+
+
+def test_prefill_select_bad_page_and_slot_ids_stay_in_bounds(msa):
+    """Inputs outside the contract: a visible block whose page id lies outside
+    [0, P) in one request's table row, and a slot id past the table in
+    another request.  The call reads nothing outside its tensors (the kernels
+    check both before any load) and the other requests' rows are exact."""
+    pb = synth.prefill_batch("bad_ids", new_tokens=[150, 100, 90, 70], prefix=[900, 1300, 600, 2000],
+                             Hq=4, Di=128, block_size_q=64, topk=5, init_blocks=1, local_blocks=1,
+                             seed=4308)
+    cu = pb.cu_seqblocks_q.numpy()
+    good_rows = np.zeros((pb.Hq, pb.all_qb), dtype=bool)
+    for b in (0, 3):
+        good_rows[:, cu[b]:cu[b + 1]] = True
+    ref, sc = reference(pb, rows=good_rows)
+    bt = pb.block_table.clone()
+    s1 = int(pb.slot_ids[1])
+    bt[s1, 2] = -1                          # visible blocks of request 1
+    bt[s1, 5] = pb.P + 3
+    d = upload(pb)
+    d["block_table"] = bt.cuda()
+    d["slot_ids"][2] = bt.shape[0] + 7      # request 2: a slot past the table
+    out = run(msa, pb, d)
+    check_prefill(pb, out, ref, sc, rows=good_rows)
+    g = out.cpu().numpy()
+    assert ((g >= -1) & (g < pb.MB)).all()  # every cell written, ids in range or -1
