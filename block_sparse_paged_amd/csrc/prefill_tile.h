@@ -246,6 +246,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
             f32x4 acc[2][QT];
             uint4 af[2][KS];
             prefill_frag<DI>(buf, 0, li, grp, af[0]);
+            // a raised issue priority while the wave streams its MFMAs: the
+            // other wave of the SIMD takes the gaps for its loads, decodes and
+            // maxima instead of interleaving with them (measured 3-4 % faster)
+            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
             for (int kt = 0; kt <= 8; ++kt) {
                 if (kt + 1 < 8) prefill_frag<DI>(buf, kt + 1, li, grp, af[(kt + 1) & 1]);
@@ -259,6 +263,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
                     }
                 }
             }
+            __builtin_amdgcn_s_setprio(0);
         } else {                                           // visibility edge: mask key >= V(column)
             int lim[QT];
 #pragma unroll
