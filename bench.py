@@ -317,20 +317,10 @@ def bf16_kv_attention(torch, msa, case, topk, copies: int = 4, reps: int = 50) -
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4)}}
 
 
-def time_sparse_decode(torch, msa, case, pools, tk, out_dtype, copies: int, reps: int) -> float:
-    """Seconds per msa_sparse_decode over `pools` [(k_cache, v_cache)] rotated in
-    a graph (cold copies), selection tensor `tk` on the device."""
-    dev = "cuda"
-    q, bt, sl = case.q.to(dev), case.block_table.to(dev), case.seq_lens.to(dev)
-    out = torch.empty((case.N, case.Hq, case.D), dtype=out_dtype, device=dev)
-    ws = torch.zeros(msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D,
-                                                           tk.shape[-1]), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.Stream()
-
-    def body():
-        for kc, vc in pools:
-            msa.msa_sparse_decode(q, kc, vc, bt, sl, tk, case.T, out, case.sm_scale, case.k_scale,
-                                  case.v_scale, case.B, ws)
+def graph_seconds(torch, stream, body, calls: int, reps: int, warm: int = 5) -> float:
+    """Seconds per call of `body` (which makes `calls` calls) captured into one
+    HIP graph on `stream`, replayed `warm` times, then `reps` times between HIP
+    events recorded on that stream."""
     with torch.cuda.stream(stream):
         body()
     torch.cuda.synchronize()
@@ -338,7 +328,7 @@ def time_sparse_decode(torch, msa, case, pools, tk, out_dtype, copies: int, reps
     with torch.cuda.graph(g, stream=stream):
         body()
     with torch.cuda.stream(stream):
-        for _ in range(5):
+        for _ in range(warm):
             g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -348,7 +338,58 @@ def time_sparse_decode(torch, msa, case, pools, tk, out_dtype, copies: int, reps
             g.replay()
         e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1000.0 / (reps * len(pools))
+    return e0.elapsed_time(e1) / 1000.0 / (reps * calls)
+
+
+def time_sparse_decode(torch, msa, case, pools, tk, out_dtype, copies: int, reps: int) -> float:
+    """Seconds per msa_sparse_decode over `pools` [(k_cache, v_cache)] rotated in
+    a graph (cold copies), selection tensor `tk` on the device."""
+    dev = "cuda"
+    q, bt, sl = case.q.to(dev), case.block_table.to(dev), case.seq_lens.to(dev)
+    out = torch.empty((case.N, case.Hq, case.D), dtype=out_dtype, device=dev)
+    ws = torch.zeros(msa.msa_sparse_decode_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D,
+                                                           tk.shape[-1]), dtype=torch.uint8, device=dev)
+
+    def body():
+        for kc, vc in pools:
+            msa.msa_sparse_decode(q, kc, vc, bt, sl, tk, case.T, out, case.sm_scale, case.k_scale,
+                                  case.v_scale, case.B, ws)
+    return graph_seconds(torch, torch.cuda.Stream(), body, len(pools), reps)
+
+
+def topk_sweep(torch, msa, synth, ks=(8, 32, 128), copies: int = 8, reps: int = 25) -> dict:
+    """The whole step (msa_decode_step: score launch, then selection + attention
+    + split merge) on the same workload at the other top-k sizes, 8, 32 and all
+    128 blocks (attention over the whole context), each on its own seeded data
+    and `copies` cold pool copies."""
+    dev = "cuda"
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    res = {"workload": "msa_decode_step, 16 rows x 4 tokens, 16384 ctx, 16q/1kv heads, D=Di=128, FP8 "
+                       "caches, top-k 8 / 32 / 128 (all blocks)"}
+    for k in ks:
+        case = synth.hbm_decode(k)
+        q_idx, q = case.q_idx.to(dev), case.q.to(dev)
+        bt, sl = case.block_table.to(dev), case.seq_lens.to(dev)
+        base = (f8(case.index_k).to(dev), f8(case.k_cache).to(dev), f8(case.v_cache).to(dev))
+        pools = [base] + [tuple(x.clone() for x in base) for _ in range(copies - 1)]
+        sc = torch.empty((case.N, case.MB), device=dev)
+        tk = torch.empty((case.N, k), dtype=torch.int32, device=dev)
+        out = torch.empty((case.N, case.Hq, case.D), dtype=torch.bfloat16, device=dev)
+        ws = torch.zeros(msa.msa_decode_step_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, k),
+                         dtype=torch.uint8, device=dev)
+
+        def body():
+            for idx, kc, vc in pools:
+                msa.msa_decode_step(q_idx, idx, q, kc, vc, bt, sl, case.T, k, case.B, case.idx_scale,
+                                    case.sm_scale, case.k_scale, case.v_scale, sc, tk, out, ws)
+        t = graph_seconds(torch, torch.cuda.Stream(), body, len(pools), reps)
+        ab = algorithmic_bytes(case, tk.cpu().numpy())
+        gbs = ab["step"] / t / 1e9
+        res[f"k{k}"] = {"us": round(t * 1e6, 3), "steps_per_s": round(1.0 / t, 1),
+                        "algorithmic_bytes": ab["step"], "achieved_hbm_gbs": round(gbs, 1),
+                        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+        del pools, base, sc, tk, out, ws
+    return res
 
 
 def kv_bytes(case, sel_rows) -> int:
@@ -635,6 +676,7 @@ def main():
         res["bf16_kv_attention"] = bf16_kv_attention(torch, msa, case, tk_host)
         res["per_request_selection"] = per_request_selection(torch, msa, case)
         res["per_kv_head_selection"] = per_kv_head_selection(torch, msa, synth, case)
+        res["topk_sweep"] = topk_sweep(torch, msa, synth)
     if a.calib_copy_mib > 0:
         # the reference copy's size and the calls' algorithmic bytes, for --pmc-summary
         os.makedirs(a.calib_out, exist_ok=True)

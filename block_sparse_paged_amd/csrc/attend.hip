@@ -412,10 +412,20 @@ static int union_splits(int32_t R, int32_t T, int32_t Hkv, int32_t k) {
     return (int)(S < 1 ? 1 : S);
 }
 
-// token path: one selected page per pair of waves while k <= 64, 4 pages per workgroup
-static void token_split(int32_t k, int32_t *S, int32_t *bpw) {
-    *bpw = (k + 63) / 64;
+// token path: 4 page slots per workgroup, bpw selected pages per slot, and
+// about one workgroup per CU: S splits of the selection list per (token, KV
+// head) unit, at most kTokenMaxSplits (the last workgroup of a unit merges all
+// S partials).  A slot streams its pages back to back, so one round of
+// workgroups with several pages per slot costs less than several rounds.
+static void token_split(int64_t units, int32_t k, int32_t *S, int32_t *bpw) {
+    int64_t s = units > 0 ? (kSplitTargetWGs + units - 1) / units : 1;
+    s = s > (k + 3) / 4 ? (k + 3) / 4 : s;
+    s = s > kTokenMaxSplits ? kTokenMaxSplits : s;
+    s = s < 1 ? 1 : s;
+    *bpw = (int32_t)((k + 4 * s - 1) / (4 * s));
+    *bpw = *bpw < 1 ? 1 : *bpw;
     *S = (k + 4 * *bpw - 1) / (4 * *bpw);
+    *S = *S < 1 ? 1 : *S;
 }
 
 bool attention_uses_mfma(int q_type, int kv_type, int G) {
@@ -426,7 +436,7 @@ AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int
     AttnPlan pl;
     pl.mfma = attention_uses_mfma(q_type, kv_type, Hq / Hkv);
     if (pl.mfma) {
-        token_split(k, &pl.splits, &pl.bpw);
+        token_split((int64_t)R * T * Hkv, k, &pl.splits, &pl.bpw);
     } else {
         pl.splits = union_splits(R, T, Hkv, k);
         pl.bpw = 1;
@@ -440,7 +450,7 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // The size covers both paths (the query does not know the element types).
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k) {
     int32_t St, bpw;
-    token_split(k, &St, &bpw);
+    token_split((int64_t)R * T * Hkv, k, &St, &bpw);
     const int32_t Su = union_splits(R, T, Hkv, k);
     const size_t S = (size_t)(St > Su ? St : Su);
     const size_t N = (size_t)R * T;

@@ -236,84 +236,113 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     uint8_t *const kc[kWaveChunks] = {lk0 + wave * CB, lk1 + wave * CB};
     uint8_t *const vc[kWaveChunks] = {lv0 + wave * CB, lv1 + wave * CB};
     const int grp = lane >> 4, li = lane & 15;
-    for (int b = 0; b < bpw; ++b) {
-        const int i = e0 + pslot * bpw + b;
-        if (i >= e1) break;
-        // entry i and duplicate check against entries [0, i)  (wave-uniform)
-        int j;
-        bool dup = false;
-        if (i < 256) {
-            const int c = i >> 6;
-            const int src = c == 0 ? tkv[0] : c == 1 ? tkv[1] : c == 2 ? tkv[2] : tkv[3];
-            j = __builtin_amdgcn_readlane(src, i & 63);
+    const int64_t ksb = p.k_sb * (BF ? 2 : 1), vsb = p.v_sb * (BF ? 2 : 1);   // row strides in bytes
+
+    // The wave's pages, resolved one ahead: entry b of its slot -> K and V row
+    // addresses of its keys kbase .. kbase + WK - 1 (kbase visible).  Entries
+    // that are padding, repeats of an earlier entry, past the row's blocks,
+    // invisible to the token or mapped to no page are skipped.
+    struct PageRef {
+        const uint8_t *kp, *vp;
+        int kbase;
+    };
+    auto next_page = [&](int &b, PageRef &pr) -> bool {
+        for (; b < bpw; ++b) {
+            const int i = e0 + pslot * bpw + b;
+            if (i >= e1) break;
+            // entry i and duplicate check against entries [0, i)  (wave-uniform)
+            int j;
+            bool dup = false;
+            if (i < 256) {
+                const int c = i >> 6;
+                const int src = c == 0 ? tkv[0] : c == 1 ? tkv[1] : c == 2 ? tkv[2] : tkv[3];
+                j = __builtin_amdgcn_readlane(src, i & 63);
 #pragma unroll
-            for (int c2 = 0; c2 < 4; ++c2) dup |= __ballot(lane + 64 * c2 < i && tkv[c2] == j) != 0;
-        } else {
-            j = p.topk[trow + (int64_t)i * p.tk_si];
-            for (int c2 = 0; c2 * 64 < i; ++c2) {
-                const int idx = c2 * 64 + lane;
-                const int v = (idx < i) ? p.topk[trow + (int64_t)idx * p.tk_si] : -1;
-                dup |= __ballot(idx < i && v == j) != 0;
+                for (int c2 = 0; c2 < 4; ++c2) dup |= __ballot(lane + 64 * c2 < i && tkv[c2] == j) != 0;
+            } else {
+                j = p.topk[trow + (int64_t)i * p.tk_si];
+                for (int c2 = 0; c2 * 64 < i; ++c2) {
+                    const int idx = c2 * 64 + lane;
+                    const int v = (idx < i) ? p.topk[trow + (int64_t)idx * p.tk_si] : -1;
+                    dup |= __ballot(idx < i && v == j) != 0;
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            const int kbase = j * kBlock + half * WK;
+            if (dup || j < 0 || j >= p.MB || kbase >= vis) continue;
+            int pid;
+            if (j < 128) {
+                pid = __builtin_amdgcn_readlane(j < 64 ? btv[0] : btv[1], j & 63);
+            } else {
+                pid = p.bt[(int64_t)r * p.bt_sr + (int64_t)j * p.bt_sj];
+                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            }
+            if (pid < 0 || pid >= p.P) continue;
+            // element strides: bytes for FP8, 2 bytes per element for bf16
+            pr.kp = (const uint8_t *)p.k_cache + ((int64_t)pid * p.k_sp + (int64_t)g * p.k_sh +
+                                                  (int64_t)(half * WK) * p.k_sb) * (BF ? 2 : 1);
+            pr.vp = (const uint8_t *)p.v_cache + ((int64_t)pid * p.v_sp + (int64_t)g * p.v_sh +
+                                                  (int64_t)(half * WK) * p.v_sb) * (BF ? 2 : 1);
+            pr.kbase = kbase;
+            ++b;
+            return true;
         }
-        // this wave's keys of the page: kbase .. kbase + WK - 1 (the first visible)
-        const int kbase = j * kBlock + half * WK;
-        if (dup || j < 0 || j >= p.MB || kbase >= vis) continue;
-        int pid;
-        if (j < 128) {
-            pid = __builtin_amdgcn_readlane(j < 64 ? btv[0] : btv[1], j & 63);
-        } else {
-            pid = p.bt[(int64_t)r * p.bt_sr + (int64_t)j * p.bt_sj];
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        }
-        if (pid < 0 || pid >= p.P) continue;
-        // element strides: bytes for FP8, 2 bytes per element for bf16
-        const uint8_t *kp = (const uint8_t *)p.k_cache + ((int64_t)pid * p.k_sp + (int64_t)g * p.k_sh +
-                                                          (int64_t)(half * WK) * p.k_sb) * (BF ? 2 : 1);
-        const uint8_t *vp = (const uint8_t *)p.v_cache + ((int64_t)pid * p.v_sp + (int64_t)g * p.v_sh +
-                                                          (int64_t)(half * WK) * p.v_sb) * (BF ? 2 : 1);
-        const int64_t ksb = p.k_sb * (BF ? 2 : 1), vsb = p.v_sb * (BF ? 2 : 1);   // row strides in bytes
-        // the previous page's LDS reads have all returned before its slots are refilled
+        b = bpw;
+        return false;
+    };
+    // Issue pipeline chunk c of a page: its K sub-chunks, then its V
+    // sub-chunks.  Load l of a sub-chunk covers its keys KPL*l .. +KPL; lane ->
+    // (key KPL*l + key0 of the sub-chunk, 16-byte unit slot).  K units are
+    // swizzled by key & 7, a function of the lane alone (KPL is a multiple of
+    // 8); V units by vswz(key), which also depends on l (bit 4 of the key) but
+    // not on the sub-chunk.  The slots' earlier LDS reads have all returned
+    // first (the compiler does not see these writes).
+    const int key0 = lane / CPR, slot = lane % CPR;
+    auto issue_chunk = [&](const PageRef &pr, int c) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        // Issue the K and V rows of the page.  Load l of a 32-key sub-chunk
-        // covers its keys KPL*l .. +KPL; lane -> (key KPL*l + key0 of the
-        // sub-chunk, 16-byte unit slot).  K units are swizzled by key & 7, a
-        // function of the lane alone (KPL is a multiple of 8); V units by
-        // vswz(key), which also depends on l (bit 4 of the key) but not on the
-        // sub-chunk.  Order: per pipeline chunk, its K sub-chunks then its V
-        // sub-chunks.
-        {
-            const int key0 = lane / CPR, slot = lane % CPR;
-            const uint8_t *ka = kp + (int64_t)key0 * ksb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
-            auto issue_k = [&](int sc) {
+        const uint8_t *ka = pr.kp + (int64_t)key0 * ksb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
 #pragma unroll
-                for (int l = 0; l < LPC; ++l) {
-                    if constexpr (BF) {
-                        const int key = l * KPL + key0;
-                        dma16_nt(kp + (int64_t)(sc * CHK + key) * ksb + ((slot ^ (key & (CPR - 1))) << 4),
-                                 kc[sc] + l * 1024);
-                    } else {
-                        dma16_nt(ka + (int64_t)(sc * kChunk + l * KPL) * ksb, kc[sc] + l * 1024);
-                    }
-                }
-            };
-            auto issue_v = [&](int sc) {
+        for (int u = 0; u < NS; ++u) {
+            const int sc = c * NS + u;
 #pragma unroll
-                for (int l = 0; l < LPC; ++l) {
+            for (int l = 0; l < LPC; ++l) {
+                if constexpr (BF) {
                     const int key = l * KPL + key0;
-                    const int sw = BF ? (key & (CPR - 1)) : (vswz(key) & (CPR - 1));
-                    dma16_nt(vp + (int64_t)(sc * CHK + key) * vsb + ((slot ^ sw) << 4), vc[sc] + l * 1024);
+                    dma16_nt(pr.kp + (int64_t)(sc * CHK + key) * ksb + ((slot ^ (key & (CPR - 1))) << 4),
+                             kc[sc] + l * 1024);
+                } else {
+                    dma16_nt(ka + (int64_t)(sc * kChunk + l * KPL) * ksb, kc[sc] + l * 1024);
                 }
-            };
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-#pragma unroll
-                for (int u = 0; u < NS; ++u) issue_k(c * NS + u);
-#pragma unroll
-                for (int u = 0; u < NS; ++u) issue_v(c * NS + u);
             }
         }
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int sc = c * NS + u;
+#pragma unroll
+            for (int l = 0; l < LPC; ++l) {
+                const int key = l * KPL + key0;
+                const int sw = BF ? (key & (CPR - 1)) : (vswz(key) & (CPR - 1));
+                dma16_nt(pr.vp + (int64_t)(sc * CHK + key) * vsb + ((slot ^ sw) << 4), vc[sc] + l * 1024);
+            }
+        }
+    };
+    // With two or more pipeline chunks per page the chunk buffers roll over
+    // pages: once chunk c of a page has been multiplied, its slots take chunk
+    // c of the wave's next page, so a wave with several pages keeps about a
+    // page of loads in flight instead of draining the queue at each page.
+    constexpr bool kRoll = NC >= 2;
+    int b = 0;
+    PageRef cur;
+    bool have = next_page(b, cur);
+    if (have) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) issue_chunk(cur, c);
+    }
+    while (have) {
+        PageRef nxt{nullptr, nullptr, 0};
+        const bool have_n = next_page(b, nxt);
+        const bool roll = kRoll && have_n;             // next page's chunks issued in the loop
+        const int kbase = cur.kbase;
         const bool full = kbase + WK <= vis;           // every key visible to this token
         // V rows past seq_len hold arbitrary bytes (NaN poison in the tests);
         // their P is 0, but 0 * NaN would poison the sum, so such keys are
@@ -322,12 +351,15 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         const bool vfull = vvalid >= WK;
         static_for<0, NC>([&](auto C) {
             constexpr int c = decltype(C)::value;
-            // loads issued after the last K (V) load of chunk c
+            // loads issued after the last K (V) load of chunk c: the page's
+            // later loads, plus chunks 0 .. c-1 of the next page when they roll
             constexpr int CL = NS * LPC;               // loads per chunk per tensor
             constexpr int after_k = CL + 2 * CL * (NC - 1 - c);
             constexpr int after_v = 2 * CL * (NC - 1 - c);
+            constexpr int ahead = 2 * CL * c;
             // ---- K rows of chunk c landed
-            wait_vmcnt<after_k>();
+            if (roll) wait_vmcnt<after_k + ahead>();
+            else wait_vmcnt<after_k>();
             // S^T tiles: sacc[u][e] = q . k for key c*CK + 16*u + 4*grp + e and
             // head h0 + lane%16.  A operand: key 16*(u%2) + lane%16 of sub-chunk
             // c*NS + u/2, d = (D/4)*grp + 8*ks .. +8
@@ -396,7 +428,8 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
             // ---- V rows of chunk c landed
-            wait_vmcnt<after_v>();
+            if (roll) wait_vmcnt<after_v + ahead>();
+            else wait_vmcnt<after_v>();
             const uint4 bp = make_uint4(pb[0][0], pb[0][1], pb[1][0], pb[1][1]);
             if constexpr (BF) {
                 // V^T A operand of the 32-key chunk: k index 8*grp + e holds key
@@ -453,7 +486,14 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                                                                     __builtin_bit_cast(bf16x8, bp), o[dt], 0, 0, 0);
                 }
             }
+            if (roll) issue_chunk(nxt, c);
         });
+        if (!kRoll && have_n) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) issue_chunk(nxt, c);
+        }
+        cur = nxt;
+        have = have_n;
     }
     // full per-head sum over the wave's four lane groups
     float l_tot = l_run + __shfl_xor(l_run, 16);
