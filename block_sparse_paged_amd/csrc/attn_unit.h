@@ -518,20 +518,26 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     __syncthreads();
     const int wm = wave;                               // the tile this thread merges
     const bool active = wm < DT;
-    float mw[NW], mx = -INFINITY;
+    // every LDS read first (one wait), then the weighted sums
+    float mw[NW], lw[NW], mx = -INFINITY;
+    f32x4 ow[NW];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) { mw[w] = smm[w * 16 + li]; mx = fmaxf(mx, mw[w]); }
+    for (int w = 0; w < NW; ++w) {
+        mw[w] = smm[w * 16 + li];
+        lw[w] = sml[w * 16 + li];
+        ow[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (active) ow[w] = *(const f32x4 *)((w < 4 ? lk0 : lk1) + (w & 3) * DT * 1024 + lane * 16 + wm * 1024);
+    }
+#pragma unroll
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, mw[w]);
     f32x4 acc4 = {0.f, 0.f, 0.f, 0.f};
     float lm = 0.f;
     if (mx != -INFINITY) {
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
             const float wgt = exp2_fast(mw[w] - mx);       // -inf -> 0
-            lm += wgt * sml[w * 16 + li];
-            if (active) {
-                const uint8_t *orow = (w < 4 ? lk0 : lk1) + (w & 3) * DT * 1024 + lane * 16;
-                acc4 += wgt * *(const f32x4 *)(orow + wm * 1024);
-            }
+            lm += wgt * lw[w];
+            acc4 += wgt * ow[w];
         }
     }
     const int h = h0 + li;
