@@ -26,7 +26,9 @@ constexpr int kPipeKeys = 32;              // keys per pipeline chunk (one softm
 // take its first and second 64 keys.  For each of its pages a wave
 //   issues its 64 K and 64 V rows straight from HBM into its LDS slots with
 //           direct-to-LDS 16-byte non-temporal loads (16-byte units
-//           XOR-swizzled by key), all at once;
+//           XOR-swizzled by key): the first page's all at once, each later
+//           page's chunk by chunk as the previous page's chunk in the same
+//           slots has been multiplied;
 //   then, per pipeline chunk of kPipeKeys keys, as soon as its K rows have
 //           landed: S^T = K Q^T on MFMA (K rows decoded FP8 -> bf16 as A
 //           operands, the 16 heads of the token as the 16 columns) and the
