@@ -54,6 +54,22 @@ def test_selection_per_kv_head(msa, spec):
     check_attention(out, oracle_attention(c, tk))
 
 
+def test_selection_per_kv_head_full_size_sampled(msa):
+    """The launch configuration of the timed 2-KV-head variant: 16 rows x 4
+    tokens at 16384 context, 32 query / 2 KV heads, one random selection of 16
+    visible blocks per KV head (128 token-head units: 2 splits of 8 pages per
+    token), checked against the oracle on 16 sampled tokens."""
+    c = synth.make_case("per_head_full", R=16, T=4, Hq=32, Hkv=2, D=128, Di=128,
+                        seq_lens=[16384] * 16, P=4096, k=16, seed=63)
+    print("case per_head_full", flush=True)
+    d = upload(c)
+    tk = per_head_topk(c, seeds=range(64, 64 + c.Hkv))
+    out = attend(msa, c, d, torch.from_numpy(tk).cuda())
+    ref = oracle_attention(c, tk, n_range=(0, 8))
+    ref[56:64] = oracle_attention(c, tk, n_range=(56, 64))[56:64]
+    check_attention(out, ref, rows=list(range(8)) + list(range(56, 64)))
+
+
 def test_selection_per_kv_head_identical_heads_equal_shared(msa):
     """[Hkv, N, k] holding the same selection for every KV head gives the
     shared-selection result bit for bit (also through non-contiguous views)."""
