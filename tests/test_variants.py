@@ -258,3 +258,49 @@ def test_per_request_shapes_checked(msa):
                             big.idx_scale, poisoned((big.R, big.MB), torch.float32))
     torch.cuda.synchronize()
     assert torch.isnan(out.float()).all()
+
+
+SAMPLED = list(range(8)) + list(range(56, 64))   # tokens of rows 0, 1, 14 and 15
+
+
+def _sampled_ref(c, tk):
+    ref = oracle_attention(c, tk, n_range=(0, 8))
+    ref[56:64] = oracle_attention(c, tk, n_range=(56, 64))[56:64]
+    return ref
+
+
+def test_bf16_kv_cache_full_size_sampled(msa):
+    """The timed dense-bf16 variant: the 16-row, 16384-context decode batch with
+    its K/V caches widened exactly to bf16, a random selection of 16 visible
+    blocks per token; the oracle of the FP8 batch (same values) on 16 tokens."""
+    c = synth.hbm_decode(16)
+    print("case bf16kv_full", flush=True)
+    d = upload(c)
+    kc, vc = d.k_cache.to(torch.bfloat16), d.v_cache.to(torch.bfloat16)
+    tk = synth.random_topk(c, seed=81)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_sparse_decode(d.q, kc, vc, d.block_table, d.seq_lens, tk.cuda(), c.T, out, c.sm_scale,
+                          c.k_scale, c.v_scale, c.B, workspace(msa, c, c.k))
+    torch.cuda.synchronize()
+    check_attention(out, _sampled_ref(c, tk.numpy()), rows=SAMPLED)
+
+
+def test_per_request_full_size_sampled(msa):
+    """The timed per-request variant: the 16-row, 16384-context decode batch,
+    its [16, 128] per-request sheet, top-16 per request, attention with the
+    selection shared by each request's 4 tokens; oracle on 16 tokens."""
+    import oracle
+    c = synth.hbm_decode(16)
+    print("case per_request_full", flush=True)
+    d = upload(c)
+    scores = poisoned((c.R, c.MB), torch.float32)
+    msa.msa_block_score(d.q_idx, d.index_k, d.block_table, d.seq_lens, c.T, c.B, c.idx_scale, scores)
+    tk = poisoned((c.R, c.k), torch.int32)
+    msa.msa_select_topk(scores, c.k, tk)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_sparse_decode(d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens, tk, c.T, out, c.sm_scale,
+                          c.k_scale, c.v_scale, c.B, workspace(msa, c, c.k))
+    torch.cuda.synchronize()
+    gs, gt = scores.cpu().numpy(), tk.cpu().numpy()
+    assert np.array_equal(gt, oracle.select_topk(gs.astype(np.float64), c.k))
+    check_attention(out, _sampled_ref(c, gt), rows=SAMPLED)
