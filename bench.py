@@ -19,6 +19,12 @@ attention launch of the step (msa_select_sparse_decode timed on its own the
 same way): its algorithmic bytes over its duration.  The CPU baseline is the
 oracle (plain C, fp64) running full steps of the same batch on the host cores.
 
+Also in the line: the same step on one pool copy (cache-resident, not an HBM
+figure), the streaming rates of library kernels on the same GPU, the step at
+top-k 8, 32 and 128, the prefill score sheet and the ragged prefill call
+(MFMA rooflines), and the attention variants (dense bf16 caches, one
+selection per request, one per KV head).
+
 Prints one JSON line.
 """
 from __future__ import annotations
