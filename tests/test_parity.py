@@ -171,6 +171,7 @@ SMALL = [
     dict(R=2, T=600, lens=(700, 1900), k=5),        # two 512-token query chunks, ragged
     dict(R=2, T=4, lens=(600, 900), k=4, Hq=32),     # 2 KV heads via Hkv below
     dict(R=4, T=64, lens=(2000, 6000, 600, 9000), k=24),   # 256 tokens: one split, 6 pages per slot
+    dict(R=1, T=4, lens=(40000,), k=300),            # 313 blocks: ids past 127, entries past 255
 ]
 
 
