@@ -91,6 +91,7 @@ BF16_KV = [
     dict(R=3, T=4, Hq=16, Hkv=1, D=64, Di=64, seq_lens=[129, 2000, 3333], P=50, k=9, qbf16=True),
     dict(R=2, T=4, Hq=32, Hkv=2, D=128, Di=128, seq_lens=[1000, 4000], P=45, k=16, qbf16=True),
     dict(R=1, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[16000], P=130, k=40, qbf16=True),
+    dict(R=1, T=4, Hq=16, Hkv=1, D=128, Di=128, seq_lens=[40000], P=318, k=300, qbf16=True),
     # vector path (f32 queries, 4 query heads per KV head)
     dict(R=2, T=3, Hq=8, Hkv=2, D=64, Di=64, seq_lens=[600, 1300], P=20, k=4, qbf16=False),
 ]
@@ -107,7 +108,8 @@ def bf16_case(spec, seed):
     return c
 
 
-@pytest.mark.parametrize("spec", BF16_KV, ids=["d128", "d64_ragged", "hkv2_k16", "k40_16k", "valu_f32q"])
+@pytest.mark.parametrize("spec", BF16_KV, ids=["d128", "d64_ragged", "hkv2_k16", "k40_16k", "k300_313blocks",
+                                               "valu_f32q"])
 def test_bf16_kv_cache(msa, spec):
     c = bf16_case(spec, seed=65)
     print(f"case bf16kv {spec}", flush=True)
