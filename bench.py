@@ -21,7 +21,7 @@ oracle (plain C, fp64) running full steps of the same batch on the host cores.
 
 Also in the line: the same step on one pool copy (cache-resident, not an HBM
 figure), the streaming rates of library kernels on the same GPU, the step at
-top-k 8, 32 and 128, the prefill score sheet and the ragged prefill call
+top-k 8, 32 and 128 and at 1, 4, 8 and 16 rows, the prefill score sheet and the ragged prefill call
 (MFMA rooflines), and the attention variants (dense bf16 caches, one
 selection per request, one per KV head).
 
@@ -363,38 +363,59 @@ def time_sparse_decode(torch, msa, case, pools, tk, out_dtype, copies: int, reps
     return graph_seconds(torch, torch.cuda.Stream(), body, len(pools), reps)
 
 
-def topk_sweep(torch, msa, synth, ks=(8, 32, 128), copies: int = 8, reps: int = 25) -> dict:
+def time_step(torch, msa, case, copies: int = 8, reps: int = 25):
+    """Seconds per msa_decode_step on `case` over `copies` cold pool copies in a
+    graph, and the selection it made (host array)."""
+    dev = "cuda"
+    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    k = case.k
+    q_idx, q = case.q_idx.to(dev), case.q.to(dev)
+    bt, sl = case.block_table.to(dev), case.seq_lens.to(dev)
+    base = (f8(case.index_k).to(dev), f8(case.k_cache).to(dev), f8(case.v_cache).to(dev))
+    pools = [base] + [tuple(x.clone() for x in base) for _ in range(copies - 1)]
+    sc = torch.empty((case.N, case.MB), device=dev)
+    tk = torch.empty((case.N, k), dtype=torch.int32, device=dev)
+    out = torch.empty((case.N, case.Hq, case.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.zeros(msa.msa_decode_step_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, k),
+                     dtype=torch.uint8, device=dev)
+
+    def body():
+        for idx, kc, vc in pools:
+            msa.msa_decode_step(q_idx, idx, q, kc, vc, bt, sl, case.T, k, case.B, case.idx_scale,
+                                case.sm_scale, case.k_scale, case.v_scale, sc, tk, out, ws)
+    t = graph_seconds(torch, torch.cuda.Stream(), body, len(pools), reps)
+    return t, tk.cpu().numpy()
+
+
+def step_entry(case, t: float, tk) -> dict:
+    ab = algorithmic_bytes(case, tk)
+    gbs = ab["step"] / t / 1e9
+    return {"us": round(t * 1e6, 3), "steps_per_s": round(1.0 / t, 1), "algorithmic_bytes": ab["step"],
+            "achieved_hbm_gbs": round(gbs, 1), "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+
+
+def topk_sweep(torch, msa, synth, ks=(8, 32, 128)) -> dict:
     """The whole step (msa_decode_step: score launch, then selection + attention
     + split merge) on the same workload at the other top-k sizes, 8, 32 and all
     128 blocks (attention over the whole context), each on its own seeded data
-    and `copies` cold pool copies."""
-    dev = "cuda"
-    f8 = lambda t: t.view(torch.float8_e4m3fn)
+    and 8 cold pool copies."""
     res = {"workload": "msa_decode_step, 16 rows x 4 tokens, 16384 ctx, 16q/1kv heads, D=Di=128, FP8 "
                        "caches, top-k 8 / 32 / 128 (all blocks)"}
     for k in ks:
         case = synth.hbm_decode(k)
-        q_idx, q = case.q_idx.to(dev), case.q.to(dev)
-        bt, sl = case.block_table.to(dev), case.seq_lens.to(dev)
-        base = (f8(case.index_k).to(dev), f8(case.k_cache).to(dev), f8(case.v_cache).to(dev))
-        pools = [base] + [tuple(x.clone() for x in base) for _ in range(copies - 1)]
-        sc = torch.empty((case.N, case.MB), device=dev)
-        tk = torch.empty((case.N, k), dtype=torch.int32, device=dev)
-        out = torch.empty((case.N, case.Hq, case.D), dtype=torch.bfloat16, device=dev)
-        ws = torch.zeros(msa.msa_decode_step_workspace_bytes(case.R, case.T, case.Hq, case.Hkv, case.D, k),
-                         dtype=torch.uint8, device=dev)
+        res[f"k{k}"] = step_entry(case, *time_step(torch, msa, case))
+    return res
 
-        def body():
-            for idx, kc, vc in pools:
-                msa.msa_decode_step(q_idx, idx, q, kc, vc, bt, sl, case.T, k, case.B, case.idx_scale,
-                                    case.sm_scale, case.k_scale, case.v_scale, sc, tk, out, ws)
-        t = graph_seconds(torch, torch.cuda.Stream(), body, len(pools), reps)
-        ab = algorithmic_bytes(case, tk.cpu().numpy())
-        gbs = ab["step"] / t / 1e9
-        res[f"k{k}"] = {"us": round(t * 1e6, 3), "steps_per_s": round(1.0 / t, 1),
-                        "algorithmic_bytes": ab["step"], "achieved_hbm_gbs": round(gbs, 1),
-                        "pct_of_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
-        del pools, base, sc, tk, out, ws
+
+def bucket_sweep(torch, msa, synth, rows=(1, 4, 8, 16)) -> dict:
+    """The whole step at the decode buckets: R rows x 4 tokens with per-row
+    context lengths uniform in [2048, 16384], top-k 16, 8 cold pool copies
+    (small batches are bound by the launches' latency, not by HBM)."""
+    res = {"workload": "msa_decode_step, R rows x 4 tokens, context uniform in [2048, 16384], 16q/1kv "
+                       "heads, D=Di=128, FP8 caches, top-k 16"}
+    for R in rows:
+        case = synth.bucket_sweep(R)
+        res[f"r{R}"] = step_entry(case, *time_step(torch, msa, case))
     return res
 
 
@@ -742,6 +763,7 @@ def main():
         res["per_request_selection"] = per_request_selection(torch, msa, case)
         res["per_kv_head_selection"] = per_kv_head_selection(torch, msa, synth, case)
         res["topk_sweep"] = topk_sweep(torch, msa, synth)
+        res["bucket_sweep"] = bucket_sweep(torch, msa, synth)
     if a.calib_copy_mib > 0:
         # the reference copy's size and the calls' algorithmic bytes, for --pmc-summary
         os.makedirs(a.calib_out, exist_ok=True)

@@ -254,6 +254,7 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kvt);
     p.splits = plan.splits;
     p.bpw = plan.bpw;
+    p.epw = plan.epw;
     p.sm_scale = sm_scale; p.k_scale = k_scale; p.v_scale = v_scale;
     p.out = out->data; p.o_sn = out->stride[0]; p.o_sh = out->stride[1]; p.o_sd = out->stride[2];
     p.out_bf16 = out->dtype == MSA_BF16;

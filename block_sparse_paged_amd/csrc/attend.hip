@@ -413,18 +413,22 @@ static int union_splits(int32_t R, int32_t T, int32_t Hkv, int32_t k) {
 }
 
 // token path: 4 page slots per workgroup, bpw selected pages per slot, and
-// about one workgroup per CU: S splits of the selection list per (token, KV
-// head) unit, at most kTokenMaxSplits (the last workgroup of a unit merges all
-// S partials).  A slot streams its pages back to back, so one round of
-// workgroups with several pages per slot costs less than several rounds.
-static void token_split(int64_t units, int32_t k, int32_t *S, int32_t *bpw) {
+// about one workgroup per CU: S splits of epw selection entries per (token,
+// KV head) unit, at most kTokenMaxSplits (the last workgroup of a unit merges
+// all S partials).  A slot streams its pages back to back, so one round of
+// workgroups with several pages per slot costs less than several rounds; a
+// small batch takes fewer than 4 entries per split (down to one page per
+// workgroup) so that its few units still spread over many CUs.
+static void token_split(int64_t units, int32_t k, int32_t *S, int32_t *bpw, int32_t *epw) {
     int64_t s = units > 0 ? (kSplitTargetWGs + units - 1) / units : 1;
-    s = s > (k + 3) / 4 ? (k + 3) / 4 : s;
+    s = s > k ? k : s;
     s = s > kTokenMaxSplits ? kTokenMaxSplits : s;
     s = s < 1 ? 1 : s;
-    *bpw = (int32_t)((k + 4 * s - 1) / (4 * s));
-    *bpw = *bpw < 1 ? 1 : *bpw;
-    *S = (k + 4 * *bpw - 1) / (4 * *bpw);
+    int64_t e = (k + s - 1) / s;                 // entries per split
+    e = e < 1 ? 1 : e;
+    *epw = (int32_t)e;
+    *bpw = (int32_t)((e + 3) / 4);
+    *S = (int32_t)((k + e - 1) / e);
     *S = *S < 1 ? 1 : *S;
 }
 
@@ -436,10 +440,11 @@ AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int
     AttnPlan pl;
     pl.mfma = attention_uses_mfma(q_type, kv_type, Hq / Hkv);
     if (pl.mfma) {
-        token_split((int64_t)R * T * Hkv, k, &pl.splits, &pl.bpw);
+        token_split((int64_t)R * T * Hkv, k, &pl.splits, &pl.bpw, &pl.epw);
     } else {
         pl.splits = union_splits(R, T, Hkv, k);
         pl.bpw = 1;
+        pl.epw = 4;
     }
     return pl;
 }
@@ -449,8 +454,8 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // [counters N*Hkv x 256 B][(m, l) S*N*Hq pairs][acc S*N*Hq*D], each 256-byte aligned.
 // The size covers both paths (the query does not know the element types).
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k) {
-    int32_t St, bpw;
-    token_split((int64_t)R * T * Hkv, k, &St, &bpw);
+    int32_t St, bpw, epw;
+    token_split((int64_t)R * T * Hkv, k, &St, &bpw, &epw);
     const int32_t Su = union_splits(R, T, Hkv, k);
     const size_t S = (size_t)(St > Su ? St : Su);
     const size_t N = (size_t)R * T;

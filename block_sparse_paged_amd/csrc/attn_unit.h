@@ -21,8 +21,10 @@ constexpr int kPipeKeys = 32;              // keys per pipeline chunk (one softm
 
 //
 // One workgroup of 8 waves per (query token n, KV head g, split s of n's
-// selection list).  The workgroup takes selection entries s*4*bpw .. +4*bpw;
-// waves 2q and 2q+1 share page slot q (entries s*4*bpw + q*bpw .. +bpw) and
+// selection list).  The workgroup takes selection entries s*epw .. +epw
+// (epw <= 4*bpw: small batches use fewer entries per split, leaving slots
+// idle, to spread over more CUs); waves 2q and 2q+1 share page slot q
+// (entries s*epw + q*bpw .. +bpw) and
 // take its first and second 64 keys.  For each of its pages a wave
 //   issues its 64 K and 64 V rows straight from HBM into its LDS slots with
 //           direct-to-LDS 16-byte non-temporal loads (16-byte units
@@ -172,9 +174,8 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     const int pslot = wave / WPP, half = wave % WPP;
     const int bpw = p.bpw * 4 / SLOTS;          // pages per wave (the same entries per workgroup)
     const int r = n / p.T, t = n % p.T;
-    const int per_wg = SLOTS * bpw;
-    const int e0 = qs * per_wg;
-    const int e1 = min(p.k, e0 + per_wg);
+    const int e0 = qs * p.epw;                  // entries of this split (epw <= SLOTS * bpw)
+    const int e1 = min(p.k, e0 + p.epw);
     const int h0 = g * 16;
 
     // One round trip for the small inputs: seq_len, the selection row up to e1

@@ -45,7 +45,8 @@ struct AttnParams {
     int32_t *topk_out;                             // same strides as topk
     int32_t R, T, MB, P, Hq, Hkv, k;
     int32_t splits;                                // S
-    int32_t bpw;                                   // selected pages per wave (token path)
+    int32_t bpw;                                   // selected pages per page slot (token path)
+    int32_t epw;                                   // selection entries per split (token path)
     float sm_scale, k_scale, v_scale;
     // split-K partials (workspace), see part_ml_index / part_acc_index
     float *part_ml, *part_acc;
@@ -132,6 +133,7 @@ struct AttnPlan {
     bool mfma;          // per-token MFMA kernel with in-launch split merge (else union VALU + reduce)
     int32_t splits;
     int32_t bpw;
+    int32_t epw;
 };
 AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type);
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k);

@@ -192,10 +192,13 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
 
 // ------------------------------------------------------------- MFMA decode path
 
+// pages (one per wave) per workgroup: 4, or 1 when the batch has too few
+// pages to give every CU a workgroup of 4
 template <int DI>
 __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
     const int wave = threadIdx.x >> 6;
-    const int JC = (p.MB + 3) >> 2;
+    const int WPG = blockDim.x >> 6;
+    const int JC = (p.MB + WPG - 1) / WPG;
     int r, jc;
     if (p.R >= 8) {
         // workgroup b runs on XCD b % 8: the row's workgroups all go to XCD r % 8,
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
         r = blockIdx.x / JC;
         jc = blockIdx.x % JC;
     }
-    const int j = jc * 4 + wave;
+    const int j = jc * WPG + wave;
     if (j >= p.MB) return;                      // no barriers in this kernel
     score_page<DI>(p, r, j);
 }
@@ -292,10 +295,11 @@ hipError_t launch_valu(const ScoreParams &p, hipStream_t s) {
 
 template <int DI>
 hipError_t launch_mfma_decode(const ScoreParams &p, hipStream_t s) {
-    const int64_t JC = (p.MB + 3) / 4;
+    const int WPG = (int64_t)p.R * ((p.MB + 3) / 4) < kSplitTargetWGs ? 1 : 4;
+    const int64_t JC = (p.MB + WPG - 1) / WPG;
     // R >= 8: 8 XCDs x ceil(R / 8) rows each x JC (see the kernel)
     const int64_t grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * JC : (int64_t)p.R * JC;
-    hipLaunchKernelGGL((score_mfma_decode_kernel<DI>), dim3((unsigned)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((score_mfma_decode_kernel<DI>), dim3((unsigned)grid), dim3(64 * WPG), 0, s, p);
     return hipGetLastError();
 }
 
