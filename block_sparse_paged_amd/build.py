@@ -19,10 +19,20 @@ HIPCC_FLAGS = [
 ]
 
 
+BENCH_CSRC = os.path.join(PKG, "bench_csrc")
+BENCH_LIB = os.path.join(PKG, "libmsa_bench.so")
+
+
 def build(verbose: bool = False) -> str:
+    """Builds libmsa.so (the library) and libmsa_bench.so (the measurement
+    kernels bench.py calibrates with); returns the library's path."""
+    _hipcc(sorted(glob.glob(os.path.join(BENCH_CSRC, "*.hip"))), BENCH_LIB, verbose)
+    return _hipcc(sorted(glob.glob(os.path.join(CSRC, "*.hip"))), LIB, verbose)
+
+
+def _hipcc(srcs, lib: str, verbose: bool) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc, *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -34,8 +44,8 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if err.strip() and verbose:
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -363,3 +363,141 @@ def prefill_ragged(seed: int = 4100) -> PrefillBatch:
     return prefill_batch("prefill_ragged_4req", new_tokens=[2048, 1536, 1024, 512],
                          prefix=[8192, 4096, 12288, 2048], Hq=4, Di=128, block_size_q=64, topk=16,
                          init_blocks=1, local_blocks=2, P=512, seed=seed)
+
+
+# ------------------------------------------- FP8 decode pins (every E4M3FN code)
+#
+# Inputs whose exact results follow from the E4M3FN value table alone: pages
+# holding one code each, one-hot queries, a single visible key.  The values the
+# codes stand for are never computed here; the tests take them from the oracle.
+
+E4M3_FINITE_CODES = [c for c in range(256) if c not in (0x7F, 0xFF)]
+
+
+def _code_pages(n_pages: int, Di: int, first: int = 0) -> torch.Tensor:
+    """[n_pages, B, Di] uint8: page i holds code E4M3_FINITE_CODES[(first + i) % 254]
+    in every key and dimension."""
+    codes = torch.tensor([E4M3_FINITE_CODES[(first + i) % len(E4M3_FINITE_CODES)]
+                          for i in range(n_pages)], dtype=torch.uint8)
+    return codes.view(n_pages, 1, 1).expand(n_pages, BLOCK, Di).contiguous()
+
+
+def fp8_code_score_case(Di: int = 128, T: int = 4, q_f32: bool = False, idx_scale: float = 1.0,
+                        seed: int = 6100) -> Case:
+    """Block scores over pages of constant codes: 2 rows x 128 blocks, page
+    (r, j) holding finite code number 128 r + j (mod 254), so every finite code
+    is some page; row 1 ends 5 keys into its last block, whose remaining keys
+    hold the two NaN codes.  Token n's query is one-hot (1.0) at dimension
+    (7 n + 3) mod Di, so its score for block j is the value of page j's code
+    times idx_scale."""
+    R, MB = 2, 128
+    P = R * MB + 1
+    perm = _rng(seed, "perm").permutation(P).astype(np.int32)
+    bt = perm[:R * MB].reshape(R, MB).copy()
+    index_k = torch.full((P, BLOCK, Di), E4M3_NAN_CODE, dtype=torch.uint8)
+    index_k[torch.from_numpy(bt.reshape(-1).astype(np.int64))] = _code_pages(R * MB, Di)
+    lens = [MB * BLOCK, (MB - 1) * BLOCK + 5]
+    last = int(bt[1, MB - 1])
+    index_k[last, 5::2] = 0x7F
+    index_k[last, 6::2] = 0xFF
+    N = R * T
+    qi = np.zeros((N, Di), dtype=np.float32)
+    for n in range(N):
+        qi[n, (7 * n + 3) % Di] = 1.0
+    q_idx = torch.from_numpy(qi) if q_f32 else to_bf16(qi)
+    return Case(name=f"fp8_codes_score_di{Di}_t{T}", R=R, T=T, Hq=16, Hkv=1, D=128, Di=Di, P=P,
+                MB=MB, k=16, B=BLOCK, fp8=True, seq_lens=torch.tensor(lens, dtype=torch.int32),
+                block_table=torch.from_numpy(bt), q_idx=q_idx, index_k=index_k, q=None,
+                k_cache=None, v_cache=None, idx_scale=float(np.float32(idx_scale)), k_scale=1.0,
+                v_scale=1.0, sm_scale=float(np.float32(1.0 / math.sqrt(128))))
+
+
+def fp8_code_prefill_batch(Hq: int = 2, topk: int = 16) -> PrefillBatch:
+    """Ragged prefill batch over 254 shared pages of constant codes (every
+    finite E4M3FN code once, in a seeded random block order).  Request b has
+    prefix 128 (17 + b) keys and one new token (query blocks of one token), so
+    its only query block selects among the first 17 + b blocks; head 0's query
+    is +1 and head 1's -1 at one dimension, so the selections order the codes
+    by value from the top and from the bottom."""
+    Di, nb = 128, len(E4M3_FINITE_CODES)
+    g = _rng(6200, "perm")
+    order = g.permutation(nb)
+    P = nb + 1
+    index_k = torch.full((P, BLOCK, Di), 0x00, dtype=torch.uint8)
+    index_k[:nb] = _code_pages(nb, Di)[torch.from_numpy(order.astype(np.int64))]
+    batch = nb - 17
+    prefix = np.array([BLOCK * (17 + b) for b in range(batch)], dtype=np.int64)
+    MB = nb + 1
+    bt = np.full((batch, MB), nb, dtype=np.int32)       # entry nb: the spare page (new tokens)
+    bt[:, :nb] = np.arange(nb, dtype=np.int32)
+    qv = np.zeros((batch, Hq, Di), dtype=np.float32)
+    for b in range(batch):
+        for h in range(Hq):
+            qv[b, h, (5 * b + 11 * h) % Di] = 1.0 if h % 2 == 0 else -1.0
+    cu = np.arange(batch + 1, dtype=np.int32)
+    return PrefillBatch(name="fp8_codes_prefill", Hq=Hq, Di=Di, B=BLOCK, P=P, MB=MB, block_size_q=1,
+                        topk=topk, init_blocks=0, local_blocks=0, scale=1.0, q=to_bf16(qv),
+                        index_k=index_k, block_table=torch.from_numpy(bt),
+                        slot_ids=torch.arange(batch, dtype=torch.int32), cu_seqlens=torch.from_numpy(cu),
+                        seq_lens=torch.from_numpy((prefix + 1).astype(np.int32)),
+                        prefix_lens=torch.from_numpy(prefix.astype(np.int32)),
+                        cu_seqblocks_q=torch.from_numpy(cu.copy()), all_qb=batch)
+
+
+def fp8_one_key_v_case(Hq: int = 16, v_scale: float = 0.125) -> Case:
+    """Attention with one visible key per token (T = 1, seq_len 1): token r's
+    key-0 V row holds finite codes 128 r .. 128 r + 127 (mod 254) over its 128
+    dimensions, so out = v_scale * value(code) in every head.  K rows hold
+    finite codes; every other slot of the page holds the NaN code."""
+    R, D = 2, 128
+    P = R + 1
+    k_cache = torch.full((P, BLOCK, 1, D), E4M3_NAN_CODE, dtype=torch.uint8)
+    v_cache = torch.full((P, BLOCK, 1, D), E4M3_NAN_CODE, dtype=torch.uint8)
+    for r in range(R):
+        row = torch.tensor([E4M3_FINITE_CODES[(128 * r + d) % len(E4M3_FINITE_CODES)]
+                            for d in range(D)], dtype=torch.uint8)
+        v_cache[r, 0, 0] = row
+        k_cache[r, 0, 0] = row.flip(0)
+    q = to_bf16(_rng(6300, "q").standard_normal((R, Hq, D), dtype=np.float32))
+    return Case(name=f"fp8_one_key_v_h{Hq}", R=R, T=1, Hq=Hq, Hkv=1, D=D, Di=128, P=P, MB=1, k=1,
+                B=BLOCK, fp8=True, seq_lens=torch.ones(R, dtype=torch.int32),
+                block_table=torch.arange(R, dtype=torch.int32).view(R, 1), q_idx=None,
+                index_k=None, q=q, k_cache=k_cache, v_cache=v_cache, idx_scale=1.0, k_scale=1.0,
+                v_scale=float(np.float32(v_scale)), sm_scale=float(np.float32(1.0 / math.sqrt(D))))
+
+
+def fp8_k_pair_case(Hq: int = 16, v_scale: float = 0.125) -> Case:
+    """Attention with two visible keys per token (T = 1, seq_len 2) whose
+    logits are equal exactly when the K codes decode right: head h's query is
+    1.0 at dimensions 2h and 2h + 1; key 0 holds code c at both, key 1 the code
+    of 2 value(c) at 2h and +0 at 2h + 1.  V is 1.0 for key 0 and 0 for key 1,
+    so every output equals v_scale / 2.  Codes c run over every finite code
+    whose double is a finite E4M3FN value, Hq of them per token."""
+    D = 128
+    assert 2 * Hq <= D
+    vals = torch.tensor(E4M3_FINITE_CODES, dtype=torch.uint8).view(torch.float8_e4m3fn).float()
+    dbl = (2 * vals).to(torch.float8_e4m3fn)
+    ok = [i for i in range(len(vals))
+          if torch.isfinite(dbl[i].float()) and dbl[i].float() == 2 * vals[i] and abs(float(vals[i])) <= 224]
+    pairs = [(E4M3_FINITE_CODES[i], int(dbl[i].view(torch.uint8))) for i in ok]
+    R = -(-len(pairs) // Hq)
+    P = R + 1
+    k_cache = torch.full((P, BLOCK, 1, D), E4M3_NAN_CODE, dtype=torch.uint8)
+    v_cache = torch.full((P, BLOCK, 1, D), E4M3_NAN_CODE, dtype=torch.uint8)
+    qv = np.zeros((R, Hq, D), dtype=np.float32)
+    for r in range(R):
+        k_cache[r, 0:2, 0] = 0x00
+        v_cache[r, 0, 0] = 0x38                   # 1.0
+        v_cache[r, 1, 0] = 0x00
+        for h in range(Hq):
+            c, c2 = pairs[(r * Hq + h) % len(pairs)]
+            k_cache[r, 0, 0, 2 * h] = c
+            k_cache[r, 0, 0, 2 * h + 1] = c
+            k_cache[r, 1, 0, 2 * h] = c2
+            qv[r, h, 2 * h] = qv[r, h, 2 * h + 1] = 1.0
+    return Case(name=f"fp8_k_pairs_h{Hq}", R=R, T=1, Hq=Hq, Hkv=1, D=D, Di=128, P=P, MB=1, k=1,
+                B=BLOCK, fp8=True, seq_lens=torch.full((R,), 2, dtype=torch.int32),
+                block_table=torch.arange(R, dtype=torch.int32).view(R, 1), q_idx=None,
+                index_k=None, q=to_bf16(qv), k_cache=k_cache, v_cache=v_cache, idx_scale=1.0,
+                k_scale=1.0, v_scale=float(np.float32(v_scale)),
+                sm_scale=float(np.float32(1.0 / math.sqrt(D))))

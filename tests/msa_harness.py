@@ -39,8 +39,8 @@ def fp8(t: torch.Tensor) -> torch.Tensor:
 
 @dataclasses.dataclass
 class Dev:
-    q_idx: torch.Tensor
-    index_k: torch.Tensor
+    q_idx: Optional[torch.Tensor]
+    index_k: Optional[torch.Tensor]
     block_table: torch.Tensor
     seq_lens: torch.Tensor
     q: Optional[torch.Tensor]
@@ -49,7 +49,7 @@ class Dev:
 
 
 def upload(case: synth.Case) -> Dev:
-    return Dev(q_idx=dev(case.q_idx), index_k=dev(fp8(case.index_k)),
+    return Dev(q_idx=dev(case.q_idx), index_k=dev(None if case.index_k is None else fp8(case.index_k)),
                block_table=dev(case.block_table), seq_lens=dev(case.seq_lens),
                q=dev(case.q), k_cache=dev(None if case.k_cache is None else fp8(case.k_cache)),
                v_cache=dev(None if case.v_cache is None else fp8(case.v_cache)))

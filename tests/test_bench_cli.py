@@ -39,3 +39,16 @@ def test_algorithmic_bytes_by_hand():
     assert ab["decode"] == kv + qo + sel + paging
     assert ab["select_decode"] == kv + qo + sheet + sel + paging
     assert ab["step"] == ab["score"] + ab["select_decode"]
+
+
+def test_copies_time_the_requested_steps():
+    import bench
+    # the driver's request: 20 timed steps after 5 warmup steps, run exactly
+    assert bench.plan_copies(20, 5) == (5, 20, 5)
+    assert bench.plan_copies(400, 40) == (8, 400, 40)
+    for steps, warm in [(20, 5), (24, 6), (7, 0), (2000, 200), (17, 3), (1, 1)]:
+        m, s, w = bench.plan_copies(steps, warm)
+        assert m >= 5 and s % m == 0 and w % m == 0      # >= 5 cold copies, whole replays
+        assert s >= steps and w >= warm                   # never fewer than asked
+        if any(steps % c == 0 and warm % c == 0 for c in range(5, 17)):
+            assert (s, w) == (steps, warm)

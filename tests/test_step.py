@@ -82,6 +82,9 @@ CASES = {
     "small_d64": lambda: synth.small_fp8(R=2, T=4, lens=(700, 1500), k=4, D=64, Di=64),
     "fallback_tiny_fp32": lambda: synth.tiny(),
     "fallback_t40": lambda: synth.small_fp8(R=2, T=40, lens=(300, 1700), k=4),
+    # 313 blocks (MB > 128): the step selects with the top-k launch before the attention
+    "mb313_k300": lambda: synth.small_fp8(R=1, T=4, lens=(40000,), k=300),
+    "mb160_k16": lambda: synth.small_fp8(R=3, T=4, lens=(20480, 700, 19000), k=16, seed=17),
 }
 
 
