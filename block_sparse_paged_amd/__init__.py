@@ -18,6 +18,9 @@ There is no CPU fallback: importing fails when the library is missing.
     msa_decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
                     tokens_per_row, k, block_size, idx_scale, sm_scale, k_scale,
                     v_scale, scores, topk_idx, out, workspace)
+    msa_decode_step_noalloc(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
+                            tokens_per_row, k, block_size, idx_scale, sm_scale, k_scale,
+                            v_scale, scores, topk_idx, out)
     msa_prefill_block_score(q, index_k, block_table, slot_ids, cu_seqlens, seq_lens,
                             prefix_lens, block_size_q, block_size_k, topk, init_blocks,
                             local_blocks, scale, cu_seqblocks_q, out_topk, workspace)
@@ -47,7 +50,8 @@ _DTYPES = {
 }
 EXPORTS = ("msa_block_score", "msa_select_topk", "msa_sparse_decode_workspace_bytes",
            "msa_sparse_decode", "msa_select_sparse_decode", "msa_decode_step_workspace_bytes",
-           "msa_decode_step", "msa_prefill_block_score_workspace_bytes", "msa_prefill_block_score",
+           "msa_decode_step", "msa_decode_step_noalloc", "msa_prefill_block_score_workspace_bytes",
+           "msa_prefill_block_score",
            "msa_get_last_error", "msa_error_string")
 
 
@@ -85,6 +89,9 @@ def _load() -> ctypes.CDLL:
     lib.msa_decode_step.restype = None
     lib.msa_decode_step.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, f32, f32, f32, f32, P, P, P,
                                     vp, sz, vp]
+    lib.msa_decode_step_noalloc.restype = None
+    lib.msa_decode_step_noalloc.argtypes = [P, P, P, P, P, P, P, i32, i32, i32, f32, f32, f32, f32, P, P,
+                                            P, vp]
     lib.msa_prefill_block_score_workspace_bytes.restype = sz
     lib.msa_prefill_block_score_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.msa_prefill_block_score.restype = None
@@ -192,6 +199,18 @@ def msa_decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
                         int(block_size), float(idx_scale), float(sm_scale), float(k_scale),
                         float(v_scale), *(ctypes.byref(x) for x in d[7:]), ws_ptr, ws_bytes,
                         _stream(stream))
+    _check()
+
+
+def msa_decode_step_noalloc(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
+                            tokens_per_row: int, k: int, block_size: int, idx_scale: float,
+                            sm_scale: float, k_scale: float, v_scale: float, scores, topk_idx, out,
+                            stream=None) -> None:
+    d = [tensor_desc(t) for t in (q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens,
+                                  scores, topk_idx, out)]
+    lib.msa_decode_step_noalloc(*(ctypes.byref(x) for x in d[:7]), int(tokens_per_row), int(k),
+                                int(block_size), float(idx_scale), float(sm_scale), float(k_scale),
+                                float(v_scale), *(ctypes.byref(x) for x in d[7:]), _stream(stream))
     _check()
 
 

@@ -5,11 +5,23 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "msa.h"
 #include "msa_internal.h"
 
 using namespace msa;
+
+// Scratch of msa_decode_step_noalloc, for callers that cannot allocate: the
+// step's split partials and arrival counters (8 MiB, one array per GPU, held
+// until the process ends).  Host code never passes `scratch` itself to a
+// kernel: its device address comes from hipGetSymbolAddress (below).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+// arrival counters sit in a fixed region at its start (512 KiB, 2048 counters
+// 256 bytes apart), so that a call never finds another call's partials where
+// its counters are; every call leaves them at zero
+constexpr int32_t kScratchCounters = 2048;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
 
 namespace {
 
@@ -109,6 +121,8 @@ const char *msa_error_string(int32_t code) {
     case MSA_ERR_WORKSPACE: return "workspace missing or too small";
     case MSA_ERR_ARG: return "scalar argument out of range";
     case MSA_ERR_LAUNCH: return "kernel launch failed";
+    case MSA_ERR_SCRATCH_LIMIT: return "sizes need more scratch than msa_decode_step_noalloc holds";
+    case MSA_ERR_SCRATCH_SETUP: return "the scratch array's device address could not be obtained";
     }
     return "unknown error";
 }
@@ -376,6 +390,94 @@ int32_t prefill_workgroups() {
     return cache[dev];
 }
 
+// ---- scratch of msa_decode_step_noalloc ------------------------------------
+//
+// For callers that cannot allocate: the split partials and arrival counters
+// live in this file-scope device array (each GPU the library runs on holds its
+// own copy until the process ends).  In host code `scratch` names a host-side
+// stand-in, not the array's device address: the address is looked up once per
+// device with hipGetSymbolAddress and only that pointer is handed to kernels.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_zeroed[kMaxDevices] = {};   // a zero fill has been enqueued outside graph capture
+
+__global__ void scratch_zero_kernel(uint4 *p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// The current device's scratch address, looked up once per device (with the
+// device current) by the first call on it.  Until a zero fill of the array has
+// been enqueued outside graph capture, every call enqueues one on `stream`
+// ahead of its kernels (a kernel, so that a call being captured records no
+// memset node; a captured fill runs at each replay of that graph); after that
+// the arrival counters are zero between calls because every call's kernels
+// leave them at zero.
+int32_t scratch_for_current_device(hipStream_t stream, void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MSA_ERR_SCRATCH_SETUP;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MSA_ERR_SCRATCH_SETUP;
+        g_scratch_ptr[dev] = p;
+    }
+    if (!g_scratch_zeroed[dev]) {
+        hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &st) != hipSuccess) return MSA_ERR_SCRATCH_SETUP;
+        hipLaunchKernelGGL(scratch_zero_kernel, dim3(512), dim3(256), 0, stream, (uint4 *)g_scratch_ptr[dev],
+                           kScratchBytes / 16);
+        if (hipGetLastError() != hipSuccess) return MSA_ERR_LAUNCH;
+        if (st == hipStreamCaptureStatusNone) g_scratch_zeroed[dev] = true;
+    }
+    *out = g_scratch_ptr[dev];
+    return MSA_OK;
+}
+
+// The whole step (msa_decode_step and msa_decode_step_noalloc): validation,
+// then the launches on `stream` with the split partials and arrival counters
+// in the workspace, or with `scratch` set in the device's scratch array
+// (sizes that need more than it holds are rejected before anything is
+// enqueued).
+int32_t decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const msa_tensor *q,
+                    const msa_tensor *k_cache, const msa_tensor *v_cache, const msa_tensor *block_table,
+                    const msa_tensor *seq_lens, int32_t tokens_per_row, int32_t k, int32_t block_size,
+                    float idx_scale, float sm_scale, float k_scale, float v_scale, msa_tensor *scores,
+                    msa_tensor *topk_idx, msa_tensor *out, void *workspace, size_t workspace_bytes, bool scratch,
+                    hipStream_t stream) {
+    ScoreParams sc;
+    TopkParams tk;
+    AttnParams at;
+    AttnPlan plan;
+    int qit, kit, Di, qt, kvt, D;
+    int32_t e = prep_score(q_idx, index_k, block_table, seq_lens, tokens_per_row, block_size, idx_scale,
+                           scores, sc, qit, kit, Di);
+    if (e == MSA_OK) e = prep_topk(scores, k, topk_idx, tk);
+    if (e == MSA_OK)
+        e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row, out, sm_scale,
+                      k_scale, v_scale, block_size, at, plan, qt, kvt, D);
+    if (e == MSA_OK && k_cache->shape[0] != index_k->shape[0]) e = MSA_ERR_SHAPE;
+    if (e == MSA_OK && (bool)sc.per_row != (bool)at.sel_per_row) e = MSA_ERR_SHAPE;
+    if (e != MSA_OK) return e;
+    const int32_t N = sc.R * sc.T;
+    if (N == 0) return MSA_OK;
+    size_t need = attn_workspace_bytes(sc.R, sc.T, at.Hq, at.Hkv, D, k);
+    if (scratch) {
+        // the scratch array holds what this call's plan touches
+        need = attn_workspace_bytes_for_splits(at.splits, N, at.Hq, at.Hkv, D, kScratchCounters);
+        if (need > kScratchBytes || (int64_t)N * at.Hkv > kScratchCounters) return MSA_ERR_SCRATCH_LIMIT;
+        const int32_t se = scratch_for_current_device(stream, &workspace);
+        if (se != MSA_OK) return se;
+        workspace_bytes = kScratchBytes;
+    }
+    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) return MSA_ERR_WORKSPACE;
+    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, scratch ? kScratchCounters : 0, &at.part_ml,
+                         &at.part_acc, &at.counters);
+    if (launch_score(sc, qit, kit, Di, stream) != hipSuccess) return MSA_ERR_LAUNCH;
+    return run_select_attn(tk, at, plan, qt, kvt, D, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -429,7 +531,7 @@ void msa_sparse_decode(const msa_tensor *q, const msa_tensor *k_cache,
         set_error(MSA_ERR_WORKSPACE);
         return;
     }
-    attn_carve_workspace(workspace, p.splits, N, p.Hq, p.Hkv, D, &p.part_ml, &p.part_acc,
+    attn_carve_workspace(workspace, p.splits, N, p.Hq, p.Hkv, D, 0, &p.part_ml, &p.part_acc,
                          &p.counters);
     const int32_t r = run_attn(p, plan, qt, kvt, D, stream);
     if (r != MSA_OK) set_error(r);
@@ -465,7 +567,7 @@ void msa_select_sparse_decode(const msa_tensor *scores, int32_t k, msa_tensor *t
         set_error(MSA_ERR_WORKSPACE);
         return;
     }
-    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_ml,
+    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, 0, &at.part_ml,
                          &at.part_acc, &at.counters);
     const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);
     if (r != MSA_OK) set_error(r);
@@ -478,32 +580,23 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
                      float idx_scale, float sm_scale, float k_scale, float v_scale,
                      msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
                      void *workspace, size_t workspace_bytes, hipStream_t stream) {
-    ScoreParams sc;
-    TopkParams tk;
-    AttnParams at;
-    AttnPlan plan;
-    int qit, kit, Di, qt, kvt, D;
-    int32_t e = prep_score(q_idx, index_k, block_table, seq_lens, tokens_per_row, block_size, idx_scale,
-                           scores, sc, qit, kit, Di);
-    if (e == MSA_OK) e = prep_topk(scores, k, topk_idx, tk);
-    if (e == MSA_OK)
-        e = prep_attn(q, k_cache, v_cache, block_table, seq_lens, topk_idx, tokens_per_row, out, sm_scale,
-                      k_scale, v_scale, block_size, at, plan, qt, kvt, D);
-    if (e == MSA_OK && k_cache->shape[0] != index_k->shape[0]) e = MSA_ERR_SHAPE;
-    if (e == MSA_OK && (bool)sc.per_row != (bool)at.sel_per_row) e = MSA_ERR_SHAPE;
-    if (e != MSA_OK) { set_error(e); return; }
-    const int32_t N = sc.R * sc.T;
-    if (N == 0) return;
-    const size_t need = attn_workspace_bytes(sc.R, sc.T, at.Hq, at.Hkv, D, k);
-    if (!workspace || workspace_bytes < need || ((uintptr_t)workspace & 255u)) {
-        set_error(MSA_ERR_WORKSPACE);
-        return;
-    }
-    attn_carve_workspace(workspace, at.splits, N, at.Hq, at.Hkv, D, &at.part_ml,
-                         &at.part_acc, &at.counters);
-    if (launch_score(sc, qit, kit, Di, stream) != hipSuccess) { set_error(MSA_ERR_LAUNCH); return; }
-    const int32_t r = run_select_attn(tk, at, plan, qt, kvt, D, stream);
-    if (r != MSA_OK) set_error(r);
+    const int32_t e = decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens, tokens_per_row, k,
+                                  block_size, idx_scale, sm_scale, k_scale, v_scale, scores, topk_idx, out,
+                                  workspace, workspace_bytes, false, stream);
+    if (e != MSA_OK) set_error(e);
+}
+
+void msa_decode_step_noalloc(const msa_tensor *q_idx, const msa_tensor *index_k, const msa_tensor *q,
+                             const msa_tensor *k_cache, const msa_tensor *v_cache,
+                             const msa_tensor *block_table, const msa_tensor *seq_lens,
+                             int32_t tokens_per_row, int32_t k, int32_t block_size,
+                             float idx_scale, float sm_scale, float k_scale, float v_scale,
+                             msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
+                             hipStream_t stream) {
+    const int32_t e = decode_step(q_idx, index_k, q, k_cache, v_cache, block_table, seq_lens, tokens_per_row, k,
+                                  block_size, idx_scale, sm_scale, k_scale, v_scale, scores, topk_idx, out,
+                                  nullptr, 0, true, stream);
+    if (e != MSA_OK) set_error(e);
 }
 
 size_t msa_prefill_block_score_workspace_bytes(int32_t batch, int32_t num_q_heads, int32_t all_seqblock_q,

@@ -463,12 +463,24 @@ size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32
     return N * Hkv * kCounterStride * 4 + align256(rows * 8) + align256(rows * D * 4);
 }
 
-void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                          float **ml, float **acc, int32_t **counters) {
+// The same layout for a plan with S splits (what the call actually touches),
+// with room for at least `counter_slots` arrival counters.
+size_t attn_workspace_bytes_for_splits(int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t counter_slots) {
     const size_t rows = (size_t)S * N * Hq;
+    const size_t ctr = (size_t)(N * Hkv > counter_slots ? N * Hkv : counter_slots);
+    return ctr * kCounterStride * 4 + align256(rows * 8) + align256(rows * D * 4);
+}
+
+// counter_slots: the counter region holds max(N*Hkv, counter_slots) counters
+// (a fixed region keeps the counters of calls of different sizes in one place)
+void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                          int32_t counter_slots, float **ml, float **acc, int32_t **counters) {
+    const size_t rows = (size_t)S * N * Hq;
+    const size_t ctr = (size_t)(N * Hkv > counter_slots ? N * Hkv : counter_slots);
     char *b = (char *)ws;
     *counters = (int32_t *)b;
-    b += (size_t)N * Hkv * kCounterStride * 4;
+    b += ctr * kCounterStride * 4;
     *ml = (float *)b;
     *acc = (float *)(b + align256(rows * 8));
     (void)D;

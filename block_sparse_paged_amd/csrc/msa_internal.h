@@ -137,8 +137,10 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type);
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k);
+size_t attn_workspace_bytes_for_splits(int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
+                                       int32_t counter_slots);
 void attn_carve_workspace(void *ws, int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
-                          float **ml, float **acc, int32_t **counters);
+                          int32_t counter_slots, float **ml, float **acc, int32_t **counters);
 
 // Launchers return hipSuccess or the launch error; dispatch on element types.
 hipError_t launch_score(const ScoreParams &p, int q_type, int k_type, int Di, hipStream_t s);

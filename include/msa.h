@@ -71,7 +71,11 @@ typedef enum msa_status {
     MSA_ERR_UNSUPPORTED = 5,   /* block size, head dim, group size, k, ... not served */
     MSA_ERR_WORKSPACE = 6,     /* workspace missing or smaller than required          */
     MSA_ERR_ARG = 7,           /* a scalar argument is out of range                   */
-    MSA_ERR_LAUNCH = 8         /* the HIP runtime refused a launch                    */
+    MSA_ERR_LAUNCH = 8,        /* the HIP runtime refused a launch                    */
+    MSA_ERR_SCRATCH_LIMIT = 9, /* msa_decode_step_noalloc: sizes need more than its
+                                  8 MiB of scratch                                    */
+    MSA_ERR_SCRATCH_SETUP = 10 /* msa_decode_step_noalloc: the scratch array's device
+                                  address could not be obtained                       */
 } msa_status;
 
 /*
@@ -232,6 +236,32 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
                      float idx_scale, float sm_scale, float k_scale, float v_scale,
                      msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
                      void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msa_decode_step without a workspace argument, for callers that cannot
+ * allocate device memory (code under graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (less the workspace),
+ * domain and outputs as msa_decode_step, bit-identical to it.
+ *
+ * The step's scratch (split partials and arrival counters) lives in an 8 MiB
+ * device array inside the library, one per GPU, held until the process ends.
+ * A call whose split plan needs more (with 16 query heads of dim 128: more
+ * than about 900 query tokens, 8 KiB of partials each; at most 2048 query
+ * tokens x KV heads) is rejected with MSA_ERR_SCRATCH_LIMIT before anything
+ * is enqueued.  The first call on a device
+ * looks the array's address up and enqueues a kernel that zero-fills it on
+ * `stream`; every call leaves its counters at zero again.  Nothing here calls
+ * hipMalloc, hipFree or an allocating library routine.  All calls on one GPU
+ * share the array: calls that overlap in time on one GPU (other streams,
+ * other threads) race and must be serialised by the caller.
+ */
+void msa_decode_step_noalloc(const msa_tensor *q_idx, const msa_tensor *index_k, const msa_tensor *q,
+                             const msa_tensor *k_cache, const msa_tensor *v_cache,
+                             const msa_tensor *block_table, const msa_tensor *seq_lens,
+                             int32_t tokens_per_row, int32_t k, int32_t block_size,
+                             float idx_scale, float sm_scale, float k_scale, float v_scale,
+                             msa_tensor *scores, msa_tensor *topk_idx, msa_tensor *out,
+                             hipStream_t stream);
 
 /*
  * Workspace bytes msa_prefill_block_score needs: one arrival counter per

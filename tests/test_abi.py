@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(msa):
 
 
 def test_error_strings(msa):
-    for code in range(0, 9):
+    for code in range(0, 11):
         s = msa.lib.msa_error_string(code)
         assert s and isinstance(s, bytes)
     assert msa.lib.msa_get_last_error() == 0
