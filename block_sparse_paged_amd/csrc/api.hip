@@ -265,7 +265,8 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     p.sel_per_row = sel_per_row;
     p.R = (int32_t)R; p.T = tokens_per_row; p.MB = (int32_t)MB; p.P = (int32_t)P;
     p.Hq = (int32_t)Hq; p.Hkv = (int32_t)Hkv; p.k = (int32_t)K;
-    plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)K, qt, kvt);
+    plan = attn_plan((int32_t)R, tokens_per_row, (int32_t)Hq, (int32_t)Hkv, (int32_t)D, (int32_t)MB, (int32_t)K,
+                     sel_per_row, sm_scale * k_scale, qt, kvt);
     p.splits = plan.splits;
     p.bpw = plan.bpw;
     p.epw = plan.epw;
@@ -275,10 +276,10 @@ int32_t prep_attn(const msa_tensor *q, const msa_tensor *k_cache, const msa_tens
     return MSA_OK;
 }
 
-// the merge kernel over the split partials the VALU attention launch left
-// (the MFMA launch merges its splits itself)
+// the merge kernel over the split partials the VALU and row-level attention
+// launches left (the per-token MFMA launch merges its splits itself)
 int32_t run_merge(const AttnParams &p, const AttnPlan &plan, int D, hipStream_t stream) {
-    if (plan.mfma) return MSA_OK;
+    if (plan.mfma && !plan.row) return MSA_OK;
     ReduceParams rp{};
     rp.part_ml = p.part_ml; rp.part_acc = p.part_acc;
     rp.out = p.out; rp.o_sn = p.o_sn; rp.o_sh = p.o_sh; rp.o_sd = p.o_sd;
@@ -290,7 +291,8 @@ int32_t run_merge(const AttnParams &p, const AttnPlan &plan, int D, hipStream_t 
 
 // attention + merge with the workspace already carved
 int32_t run_attn(AttnParams &p, const AttnPlan &plan, int qt, int kvt, int D, hipStream_t stream) {
-    if (launch_attention(p, qt, kvt, D, stream) != hipSuccess) return MSA_ERR_LAUNCH;
+    const hipError_t le = plan.row ? launch_attention_row(p, D, false, stream) : launch_attention(p, qt, kvt, D, stream);
+    if (le != hipSuccess) return MSA_ERR_LAUNCH;
     return run_merge(p, plan, D, stream);
 }
 
@@ -304,6 +306,10 @@ int32_t run_select_attn(const TopkParams &tk, AttnParams &at, const AttnPlan &pl
     if (plan.mfma && tk.MB <= kSelectInAttnMaxMB) {
         at.scores = tk.scores; at.sc_sn = tk.sc_sn; at.sc_sj = tk.sc_sj;
         at.topk_out = tk.topk;
+        if (plan.row) {
+            if (launch_attention_row(at, D, true, stream) != hipSuccess) return MSA_ERR_LAUNCH;
+            return run_merge(at, plan, D, stream);
+        }
         return launch_attention_select(at, D, kvt, stream) == hipSuccess ? MSA_OK : MSA_ERR_LAUNCH;
     }
     if (launch_topk(tk, stream) != hipSuccess) return MSA_ERR_LAUNCH;

@@ -297,69 +297,104 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 
 // ------------------------------------------------------------------ reduction
 
-// Split merge: one thread per (query token, head, 8 consecutive d).  All of a
-// chunk's partial loads are issued before they are combined; splits are folded
-// in increasing order (deterministic).  A split that saw no key has m = -inf
-// and its acc is never read into the sum.
-__global__ __launch_bounds__(256) void attn_reduce_kernel(ReduceParams p) {
+// Split merge: four threads per (query token, head, 8 consecutive d), thread
+// group q of the workgroup folding splits q, q + 4, q + 8, ... (all of its
+// partial loads issued before they are combined, so that a merge costs about
+// one memory round trip whatever the split count), then the four groups'
+// results combined in group order through LDS.  The order is fixed
+// (deterministic).  A split that saw no key has m = -inf and its acc is never
+// read into the sum.
+constexpr int kReduceOuts = 64;              // outputs (8-wide d groups) per workgroup
+constexpr int kReduceGroups = 4;             // split groups per output
+
+struct Fold {
+    float m, l, a[8];
+};
+
+__device__ __forceinline__ void fold_in(Fold &f, float mu, float lu, const f32x4 &lo, const f32x4 &hi) {
+    // mu = -inf: nothing to add (acc not read)
+    const bool live = mu != -INFINITY;
+    const float mn = fmaxf(f.m, live ? mu : -INFINITY);
+    const float wo = (f.m == -INFINITY) ? 0.f : exp2_fast(f.m - mn);
+    const float wn = live ? exp2_fast(mu - mn) : 0.f;
+    f.l = f.l * wo + (live ? lu : 0.f) * wn;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        f.a[e] = f.a[e] * wo + (live ? lo[e] : 0.f) * wn;
+        f.a[4 + e] = f.a[4 + e] * wo + (live ? hi[e] : 0.f) * wn;
+    }
+    f.m = mn;
+}
+
+__global__ __launch_bounds__(kReduceOuts * kReduceGroups) void attn_reduce_kernel(ReduceParams p) {
     // thread -> (token n, 8-wide d group dq, head h), h fastest: the partial
     // loads of consecutive threads are contiguous
+    __shared__ float sf[kReduceGroups - 1][10][kReduceOuts];
     const int DQ = p.D >> 3;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int o = threadIdx.x % kReduceOuts, q = threadIdx.x / kReduceOuts;
+    const int64_t idx = (int64_t)blockIdx.x * kReduceOuts + o;
     const int64_t N = p.N;
-    if (idx >= N * p.Hq * DQ) return;
-    const int h = (int)(idx % p.Hq);
-    const int dq = (int)((idx / p.Hq) % DQ);
-    const int64_t n = idx / ((int64_t)p.Hq * DQ);
-    float m2 = -INFINITY, l2 = 0.f, a2[8];
+    const bool live = idx < N * p.Hq * DQ;
+    const int h = live ? (int)(idx % p.Hq) : 0;
+    const int dq = live ? (int)((idx / p.Hq) % DQ) : 0;
+    const int64_t n = live ? idx / ((int64_t)p.Hq * DQ) : 0;
+    Fold f;
+    f.m = -INFINITY;
+    f.l = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) a2[e] = 0.f;
-    for (int s0 = 0; s0 < p.splits; s0 += 4) {
-        f32x2 ml[4];
-        f32x4 lo[4], hi[4];
+    for (int e = 0; e < 8; ++e) f.a[e] = 0.f;
+    if (live) {
+        for (int s0 = q; s0 < p.splits; s0 += 4 * kReduceGroups) {
+            f32x2 ml[4];
+            f32x4 lo[4], hi[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int sp = min(s0 + u, p.splits - 1);
-            ml[u] = *(const f32x2 *)(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
-            const f32x4 *src = (const f32x4 *)(p.part_acc + part_acc_index(sp, n, h, dq * 8, N, p.Hq, p.D));
-            lo[u] = src[0];
-            hi[u] = src[1];
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const bool live = s0 + u < p.splits && ml[u].x != -INFINITY;
-            const float mu = live ? ml[u].x : -INFINITY;
-            const float mn = fmaxf(m2, mu);
-            const float wo = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
-            const float wn = live ? exp2_fast(mu - mn) : 0.f;
-            l2 = l2 * wo + (live ? ml[u].y : 0.f) * wn;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a2[e] = a2[e] * wo + (live ? lo[u][e] : 0.f) * wn;
-                a2[4 + e] = a2[4 + e] * wo + (live ? hi[u][e] : 0.f) * wn;
+            for (int u = 0; u < 4; ++u) {
+                const int sp = min(s0 + u * kReduceGroups, p.splits - 1);
+                ml[u] = *(const f32x2 *)(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
+                const f32x4 *src = (const f32x4 *)(p.part_acc + part_acc_index(sp, n, h, dq * 8, N, p.Hq, p.D));
+                lo[u] = src[0];
+                hi[u] = src[1];
             }
-            m2 = mn;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                fold_in(f, s0 + u * kReduceGroups < p.splits ? ml[u].x : -INFINITY, ml[u].y, lo[u], hi[u]);
         }
     }
-    const float inv = (l2 > 0.f) ? p.v_scale / l2 : 0.f;
+    if (q > 0) {
+        float *d = &sf[q - 1][0][o];
+        d[0] = f.m;
+        d[kReduceOuts] = f.l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) d[(2 + e) * kReduceOuts] = f.a[e];
+    }
+    __syncthreads();
+    if (q > 0 || !live) return;
+#pragma unroll
+    for (int g = 0; g < kReduceGroups - 1; ++g) {
+        const float *d = &sf[g][0][o];
+        fold_in(f, d[0], d[kReduceOuts], f32x4{d[2 * kReduceOuts], d[3 * kReduceOuts], d[4 * kReduceOuts],
+                                               d[5 * kReduceOuts]},
+                f32x4{d[6 * kReduceOuts], d[7 * kReduceOuts], d[8 * kReduceOuts], d[9 * kReduceOuts]});
+    }
+    const float inv = (f.l > 0.f) ? p.v_scale / f.l : 0.f;
     const int64_t base = n * p.o_sn + (int64_t)h * p.o_sh + (int64_t)(dq * 8) * p.o_sd;
     if (p.out_bf16) {
         uint16_t *op = (uint16_t *)p.out;
         if (p.o_sd == 1) {
             uint4 v;
-            v.x = cvt_pk_bf16(a2[0] * inv, a2[1] * inv);
-            v.y = cvt_pk_bf16(a2[2] * inv, a2[3] * inv);
-            v.z = cvt_pk_bf16(a2[4] * inv, a2[5] * inv);
-            v.w = cvt_pk_bf16(a2[6] * inv, a2[7] * inv);
+            v.x = cvt_pk_bf16(f.a[0] * inv, f.a[1] * inv);
+            v.y = cvt_pk_bf16(f.a[2] * inv, f.a[3] * inv);
+            v.z = cvt_pk_bf16(f.a[4] * inv, f.a[5] * inv);
+            v.w = cvt_pk_bf16(f.a[6] * inv, f.a[7] * inv);
             *(uint4 *)(op + base) = v;
         } else {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) op[base + e * p.o_sd] = (uint16_t)cvt_pk_bf16(a2[e] * inv, 0.f);
+            for (int e = 0; e < 8; ++e) op[base + e * p.o_sd] = (uint16_t)cvt_pk_bf16(f.a[e] * inv, 0.f);
         }
     } else {
         float *op = (float *)p.out;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) op[base + e * p.o_sd] = a2[e] * inv;
+        for (int e = 0; e < 8; ++e) op[base + e * p.o_sd] = f.a[e] * inv;
     }
 }
 
@@ -436,10 +471,16 @@ bool attention_uses_mfma(int q_type, int kv_type, int G) {
     return G == 16 && q_type == E_BF16 && (kv_type == E_FP8 || kv_type == E_BF16);
 }
 
-AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type) {
+AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t MB, int32_t k,
+                   bool sel_per_row, float score_scale, int q_type, int kv_type) {
     AttnPlan pl;
     pl.mfma = attention_uses_mfma(q_type, kv_type, Hq / Hkv);
-    if (pl.mfma) {
+    pl.row = attention_row_eligible(q_type, kv_type, D, Hq / Hkv, T, MB, k, sel_per_row, score_scale);
+    if (pl.row) {
+        pl.splits = row_splits(R, Hkv);
+        pl.bpw = 1;
+        pl.epw = 0;
+    } else if (pl.mfma) {
         token_split((int64_t)R * T * Hkv, k, &pl.splits, &pl.bpw, &pl.epw);
     } else {
         pl.splits = union_splits(R, T, Hkv, k);
@@ -457,7 +498,9 @@ size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32
     int32_t St, bpw, epw;
     token_split((int64_t)R * T * Hkv, k, &St, &bpw, &epw);
     const int32_t Su = union_splits(R, T, Hkv, k);
-    const size_t S = (size_t)(St > Su ? St : Su);
+    size_t S = (size_t)(St > Su ? St : Su);
+    // the row-level kernel's splits (it may serve 2 <= T <= 4 with k <= 128)
+    if (T >= 2 && T <= 4 && k <= kSelSlots) S = S > (size_t)row_splits(R, Hkv) ? S : (size_t)row_splits(R, Hkv);
     const size_t N = (size_t)R * T;
     const size_t rows = S * N * Hq;
     return N * Hkv * kCounterStride * 4 + align256(rows * 8) + align256(rows * D * 4);
@@ -517,9 +560,9 @@ hipError_t launch_attention_select(const AttnParams &p, int D, int kv_type, hipS
 hipError_t launch_reduce(const ReduceParams &p, hipStream_t s) {
     const int64_t total = (int64_t)p.N * p.Hq * (p.D / 8);
     if (total == 0) return hipSuccess;
-    const int64_t grid = (total + 255) / 256;
+    const int64_t grid = (total + kReduceOuts - 1) / kReduceOuts;
     // v_scale is applied at the merge: out = v_scale * sum w acc / sum w l
-    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_reduce_kernel, dim3((unsigned)grid), dim3(kReduceOuts * kReduceGroups), 0, s, p);
     return hipGetLastError();
 }
 

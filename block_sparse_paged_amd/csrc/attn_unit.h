@@ -34,9 +34,10 @@ constexpr int kPipeKeys = 32;              // keys per pipeline chunk (one softm
 //   then, per pipeline chunk of kPipeKeys keys, as soon as its K rows have
 //           landed: S^T = K Q^T on MFMA (K rows decoded FP8 -> bf16 as A
 //           operands, the 16 heads of the token as the 16 columns) and the
-//           online-softmax update, and as soon as its V rows have landed
-//           O^T += V^T P^T, with V read back by ds_read_b64_tr_b8, which hands
-//           each lane 8 keys at one d (the A operand).
+//           online-softmax update (lazily moved reference), and as soon as
+//           its V rows have landed O^T += V^T P^T with P as two bf16 parts
+//           (two MFMAs), V read back by ds_read_b64_tr_b8, which hands each
+//           lane 8 keys at one d (the A operand).
 // The waits are explicit vmcnt counts over the wave's in-order load queue.
 // Two waves per SIMD (128 KiB of K/V slots per workgroup, one workgroup per
 // CU) let one wave's math overlap the other's.
@@ -122,6 +123,46 @@ __device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
     r.z = fp8x2_to_bf16x2<false>(hi);
     r.w = fp8x2_to_bf16x2<true>(hi);
     return r;
+}
+
+// Lazily moved softmax reference: a head's reference m moves only when a
+// chunk's max exceeds it by more than kSlack (log2 units), so that the
+// accumulators are rescaled rarely; the weights 2^(s - m) stay below 2^kSlack.
+constexpr float kSlack = 8.f;
+
+// max of a lane's 8 products of a 32-key chunk
+__device__ __forceinline__ float chunk_max(const f32x4 (&sacc)[2]) {
+    return max3f(max3f(sacc[0][0], sacc[0][1], sacc[0][2]), max3f(sacc[0][3], sacc[1][0], sacc[1][1]),
+                 fmaxf(sacc[1][2], sacc[1][3]));
+}
+
+// Softmax weights p = 2^(s - m) of a 32-key chunk (sacc[u][e]: key
+// 16*u + 4*grp + e of the lane's group) as MFMA B operands in two bf16 parts,
+// hi = bf16(p) and lo = bf16(p - hi) (p - hi is exact in fp32), so that
+// V^T P_hi^T + V^T P_lo^T carries p to about 2^-17 relative: bf16 alone
+// (2^-9) passes straight into the output of a token that sees only a few keys
+// (two keys of values -4 and 4 at equal weight: up to 4 * 2^-9 ~ 0.008).
+// `sum` is the lane's fp32 weights (hi + lo equals each to 2^-17 relative).
+struct PWeights {
+    uint4 hi, lo;
+    float sum;
+};
+__device__ __forceinline__ PWeights softmax_weights(const f32x4 (&sacc)[2], float m) {
+    uint32_t h[4], l[4];
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float a = exp2_fast(sacc[u][2 * hh] - m), b = exp2_fast(sacc[u][2 * hh + 1] - m);
+            const uint32_t w = cvt_pk_bf16(a, b);
+            const float ah = bf16lo_to_f32(w), bh = bf16hi_to_f32(w);
+            const uint32_t wl = cvt_pk_bf16(a - ah, b - bh);
+            h[2 * u + hh] = w;
+            l[2 * u + hh] = wl;
+            sum += a + b;
+        }
+    return PWeights{make_uint4(h[0], h[1], h[2], h[3]), make_uint4(l[0], l[1], l[2], l[3]), sum};
 }
 
 // BF16 caches (attention.decode's dense cache): rows of 2*D bytes, so a wave
@@ -404,36 +445,24 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                     for (int e = 0; e < 4; ++e)
                         sacc[u][e] = (kbase + c * CK + u * 16 + 4 * grp + e < vis) ? sacc[u][e] : -INFINITY;
             }
-            float cmax = -INFINITY;
+            const float cmax = max_over_lane_groups(chunk_max(sacc));
+            // lazily moved reference (a rare rescale).  Chunk 0 holds the
+            // wave's first key of the page, which is visible: m is finite from
+            // the first chunk of the first page on.
+            const bool up = cmax > m_run + kSlack;
+            if (__ballot(up)) {
+                const float alpha = up ? exp2_fast(m_run - cmax) : 1.f;
+                m_run = up ? cmax : m_run;
+                l_run *= alpha;
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                cmax = fmaxf(cmax, fmaxf(fmaxf(sacc[u][0], sacc[u][1]), fmaxf(sacc[u][2], sacc[u][3])));
-            cmax = max_across_groups<16>(cmax);
-            // chunk 0 holds the wave's first key of the page, which is visible:
-            // m_new is finite from the first chunk of the first page on
-            const float m_new = fmaxf(m_run, cmax);
-            const float alpha = exp2_fast(m_run - m_new);
-            m_run = m_new;
-            // P rounded to bf16 (hardware RNE); l sums the rounded values so
-            // that the weights used in PV and in the normaliser are the same
-            uint32_t pb[2][2];
-            float lsum = 0.f;
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-#pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const uint32_t w = cvt_pk_bf16(exp2_fast(sacc[u][2 * hh] - m_new),
-                                                   exp2_fast(sacc[u][2 * hh + 1] - m_new));
-                    pb[u][hh] = w;
-                    lsum += __uint_as_float(w << 16) + __uint_as_float(w & 0xffff0000u);
-                }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+                for (int dt = 0; dt < DT; ++dt) o[dt] *= alpha;
+            }
+            // P as two bf16 parts
+            const PWeights pw = softmax_weights(sacc, m_run);
+            l_run += pw.sum;
             // ---- V rows of chunk c landed
             if (roll) wait_vmcnt<after_v + ahead>();
             else wait_vmcnt<after_v>();
-            const uint4 bp = make_uint4(pb[0][0], pb[0][1], pb[1][0], pb[1][1]);
             if constexpr (BF) {
                 // V^T A operand of the 32-key chunk: k index 8*grp + e holds key
                 // pv_key(grp, e) = sub-chunk e/4, key 4*grp + e%4; lane li of the
@@ -461,8 +490,9 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                         (__attribute__((address_space(3))) v4i16 *)(v1 + ((unit ^ vsw) << 4))));
                     r0.x &= ~kill[0][0]; r0.y &= ~kill[0][1];
                     r1.x &= ~kill[1][0]; r1.y &= ~kill[1][1];
-                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, bf16x4x2(r0, r1)),
-                                                                    __builtin_bit_cast(bf16x8, bp), o[dt], 0, 0, 0);
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, bf16x4x2(r0, r1));
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pw.hi), o[dt], 0, 0, 0);
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pw.lo), o[dt], 0, 0, 0);
                 }
             } else {
                 // lanes 2b, 2b+1 of a 16-lane group read the two 8-byte halves of
@@ -484,9 +514,10 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                 for (int dt = 0; dt < DT; ++dt) {
                     const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                         (__attribute__((address_space(3))) v2i *)(vrow + ((dt ^ vsw) << 4)));
-                    const uint4 a = fp8x8_to_bf16x8((uint32_t)raw.x & ~kill_lo, (uint32_t)raw.y & ~kill_hi);
-                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                    __builtin_bit_cast(bf16x8, bp), o[dt], 0, 0, 0);
+                    const bf16x8 a = __builtin_bit_cast(
+                        bf16x8, fp8x8_to_bf16x8((uint32_t)raw.x & ~kill_lo, (uint32_t)raw.y & ~kill_hi));
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pw.hi), o[dt], 0, 0, 0);
+                    o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, pw.lo), o[dt], 0, 0, 0);
                 }
             }
             if (roll) issue_chunk(nxt, c);

@@ -112,6 +112,24 @@ __device__ __forceinline__ float group_max(float v) {
     return v;
 }
 
+// max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
+// first, unlike fmaxf); the operands are dot products or -inf, never NaN (a
+// NaN dot product is outside the contract)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane groups), with
+// the gfx950 lane swaps: permlane32_swap of a value with itself leaves each
+// lane holding its own value and lane l ^ 32's in the two results, and
+// permlane16_swap likewise lane l ^ 16's.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Max over lanes whose index differs only in bits >= log2(FROM) (all lanes
 // holding equal values within groups of FROM).
 template <int FROM>

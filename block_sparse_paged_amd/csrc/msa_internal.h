@@ -12,6 +12,7 @@ constexpr int kTokGroup = 4;         // query tokens of one row handled together
 constexpr int kSplitTargetWGs = 256; // attention workgroups aimed for (one per CU)
 constexpr int kTokenMaxSplits = 16;  // splits of one token's selection list (MFMA path)
 constexpr int kCounterStride = 64;   // int32s between split-arrival counters (one per 256 B)
+constexpr int kRowMaxSplits = 32;    // splits of one row's block list (row-level attention)
 
 enum ElemType { E_F32 = 0, E_BF16 = 1, E_FP8 = 2, E_I32 = 3 };
 
@@ -128,14 +129,29 @@ __host__ __device__ __forceinline__ int64_t part_acc_index(int s, int64_t n, int
 hipError_t launch_attention_select(const AttnParams &p, int D, int kv_type, hipStream_t s);
 constexpr int kSelectInAttnMaxMB = 128;
 
+// Row-level attention (attend_row.hip): one workgroup per (row, KV head,
+// split of the row's ascending list of selected blocks), each page loaded and
+// decoded once per row for all of the row's tokens that selected it; the
+// splits are merged by the reduction kernel.  Served for bf16 queries, FP8
+// K/V, 16 query heads per KV head, D 64 or 128, 2 to 4 tokens per row,
+// MB <= 128, sm_scale * k_scale > 0, and selections the tokens share (one
+// per request), or per-token selections whose expected union is at most half
+// of the pages the per-token unit would stream.
+bool attention_row_eligible(int q_type, int kv_type, int D, int G, int T, int MB, int k, bool sel_per_row,
+                            float score_scale);
+int32_t row_splits(int32_t R, int32_t Hkv);
+hipError_t launch_attention_row(const AttnParams &p, int D, bool select, hipStream_t s);
+
 // Split plan of msa_sparse_decode for the given sizes and element types.
 struct AttnPlan {
     bool mfma;          // per-token MFMA kernel with in-launch split merge (else union VALU + reduce)
+    bool row;           // row-level MFMA kernel + reduce
     int32_t splits;
     int32_t bpw;
     int32_t epw;
 };
-AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t k, int q_type, int kv_type);
+AttnPlan attn_plan(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t MB, int32_t k,
+                   bool sel_per_row, float score_scale, int q_type, int kv_type);
 size_t attn_workspace_bytes(int32_t R, int32_t T, int32_t Hq, int32_t Hkv, int32_t D, int32_t k);
 size_t attn_workspace_bytes_for_splits(int32_t S, int32_t N, int32_t Hq, int32_t Hkv, int32_t D,
                                        int32_t counter_slots);

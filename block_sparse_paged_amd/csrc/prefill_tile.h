@@ -28,13 +28,6 @@ namespace msa {
 constexpr int kPWaves = 8;        // waves per workgroup, two per SIMD
 constexpr int kPMaxPC = 8;        // blocks per tile of the prefill score sheet, at most
 
-// max of three as IEEE maximum (v_maximum3_f32, no quieting of the operands
-// first, unlike fmaxf); the operands are dot products, never NaN (a NaN dot
-// product is outside the contract)
-__device__ __forceinline__ float max3f(float a, float b, float c) {
-    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
-}
-
 // bf16 A operands of the 16-key tile kt of the page in `buf`: key 16*kt +
 // lane%16; k-step ks covers d = 32*ks .. +31, lane group grp its d = 32*ks +
 // 8*grp .. +7: 16-byte unit 4*ks + grp of the key's bf16 row, stored

@@ -228,3 +228,18 @@ def test_prefill_block_score_rejects(msa):
     _expect(msa, 6, f, *with_(15, ws[:256]))                              # too small
     _expect(msa, 6, f, *with_(15, ws[1:]))                                # misaligned
     assert (out == -7).all()
+
+
+def test_build_refuses_scratch_memory():
+    """The build reads the compiler's resource remarks and names every kernel
+    given scratch memory (the attention kernels count their own loads in the
+    wave's queue, which scratch accesses would join)."""
+    from block_sparse_paged_amd.build import scratch_users
+    remarks = "\n".join([
+        "a.hip:1:1: remark: Function Name: kern_a [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark: Function Name: kern_b [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     VGPRs: 256 [-Rpass-analysis=kernel-resource-usage]",
+        "a.hip:9:1: remark:     ScratchSize [bytes/lane]: 560 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert scratch_users(remarks) == [("kern_b", 560)]

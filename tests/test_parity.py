@@ -248,3 +248,36 @@ def test_caller_topk_with_gaps(msa):
     ref = oracle_attention(c, clean)
     check_attention(out, ref)
     assert (out[5].float().cpu() == 0).all()
+
+
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_tokens_that_see_few_keys(msa, kv):
+    """Rows of 2, 3 and 5 tokens read by 4 query tokens each (tokens that see
+    0 to 5 keys, whose outputs mix a few V rows: any rounding of the softmax
+    weights shows in them directly), on the per-token MFMA kernel with FP8 and
+    bf16 K/V caches.  Beyond the 2e-3 bound, every output must lie within one
+    bf16 step of the oracle's rounded value plus 2^-14 (outputs near zero come
+    from cancelling V rows, so their error is absolute): weights carried as a
+    single bf16 leave up to |v| * 2^-9 (about 2e-3 here) in such outputs."""
+    import oracle
+    from msa_harness import bf16_ulp, poisoned, workspace
+    c = synth.small_fp8(R=4, T=4, lens=(2, 3, 5, 3000), k=2, seed=6501)
+    _say(f"case few keys, kv {kv}: lens {c.seq_lens.tolist()} k={c.k} MB={c.MB}")
+    d = upload(c)
+    kc, vc = d.k_cache, d.v_cache
+    if kv == "bf16":
+        kc, vc = kc.to(torch.bfloat16), vc.to(torch.bfloat16)
+    tk = synth.random_topk(c, seed=6502)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_sparse_decode(d.q, kc, vc, d.block_table, d.seq_lens, tk.cuda(), c.T, out, c.sm_scale,
+                          c.k_scale, c.v_scale, c.B, workspace(msa, c, c.k))
+    torch.cuda.synchronize()
+    ref = oracle_attention(c, tk.numpy())
+    check_attention(out, ref)
+    g = out.float().cpu().double().numpy()
+    rb = oracle.round_bf16(ref)
+    excess = np.abs(g - rb) - bf16_ulp(rb)
+    worst = np.unravel_index(np.argmax(excess), excess.shape)
+    assert (excess <= 2.0 ** -14).all(), (
+        f"{int((excess > 2.0 ** -14).sum())} cells off; worst at {worst}: gpu {g[worst]!r} "
+        f"oracle {ref[worst]!r} (visible keys {c.visible(worst[0])})")
