@@ -215,10 +215,12 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_row_kernel(AttnParams
         if (tg == 0) {
             const uint8_t *kp = (const uint8_t *)p.k_cache + (int64_t)pid * p.k_sp + (int64_t)g * p.k_sh +
                                 (int64_t)(kChunk * quarter) * ksb;
-            // K units swizzled by key & 7, V units by vswz(key) (as in attn_unit.h)
-            const uint8_t *ka = kp + (int64_t)key0 * ksb + ((unit ^ (key0 & (CPR - 1) & 7)) << 4);
+            // K units swizzled by kswz(key), V units by vswz(key) (as in attn_unit.h)
 #pragma unroll
-            for (int l = 0; l < LPC; ++l) dma16_nt(ka + (int64_t)(l * KPL) * ksb, kv[0][buf][quarter] + l * 1024);
+            for (int l = 0; l < LPC; ++l) {
+                const int key = l * KPL + key0;
+                dma16_nt(kp + (int64_t)key * ksb + ((unit ^ kswz<CPR>(key)) << 4), kv[0][buf][quarter] + l * 1024);
+            }
         } else {
             const uint8_t *vp = (const uint8_t *)p.v_cache + (int64_t)pid * p.v_sp + (int64_t)g * p.v_sh +
                                 (int64_t)(kChunk * quarter) * vsb;
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_row_kernel(AttnParams
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int key = 16 * u + li;
-                const int ku = (((D / 4) * grp) / 16 + kp2) ^ (key & (CPR - 1) & 7);
+                const int ku = (((D / 4) * grp) / 16 + kp2) ^ kswz<CPR>(key);
                 const uint4 raw = *(const uint4 *)(kq + key * D + (ku << 4));
                 ka[u][0] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(raw.x, raw.y));
                 ka[u][1] = __builtin_bit_cast(bf16x8, fp8x8_to_bf16x8(raw.z, raw.w));

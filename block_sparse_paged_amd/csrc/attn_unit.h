@@ -104,6 +104,17 @@ __device__ __forceinline__ f32x2 ld_coherent2(const float *p) {
     return f32x2{__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32))};
 }
 
+// FP8 K rows in LDS (CPR 16-byte units a row): unit c of key k stored at unit
+// c ^ kswz<CPR>(k).  A ds_read_b128 serves 16 lanes a cycle from the 64 banks
+// (256 bytes); the 16 keys k0 .. k0 + 15 at one unit fall on rows whose bank
+// offset repeats every 16 / CPR keys, and kswz spreads the CPR keys of each
+// offset over distinct units, so that the 16 reads hit 16 distinct 16-byte
+// bank groups.
+template <int CPR>
+__device__ __forceinline__ int kswz(int key) {
+    return ((key * CPR) >> 4) & (CPR - 1);
+}
+
 // V rows in LDS: 16-byte unit c of key k stored at unit c ^ vswz(k).  vswz
 // separates the 8 keys one ds_read_b64_tr_b8 group touches (keys 4a..4a+3 and
 // 16+4a..16+4a+3 of a 32-key chunk) onto distinct unit positions.
@@ -336,15 +347,13 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     };
     // Issue pipeline chunk c of a page: its K sub-chunks, then its V
     // sub-chunks.  Load l of a sub-chunk covers its keys KPL*l .. +KPL; lane ->
-    // (key KPL*l + key0 of the sub-chunk, 16-byte unit slot).  K units are
-    // swizzled by key & 7, a function of the lane alone (KPL is a multiple of
-    // 8); V units by vswz(key), which also depends on l (bit 4 of the key) but
+    // (key KPL*l + key0 of the sub-chunk, 16-byte unit slot).  FP8 K units
+    // are swizzled by kswz(key), V units by vswz(key); both depend on l but
     // not on the sub-chunk.  The slots' earlier LDS reads have all returned
     // first (the compiler does not see these writes).
     const int key0 = lane / CPR, slot = lane % CPR;
     auto issue_chunk = [&](const PageRef &pr, int c) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        const uint8_t *ka = pr.kp + (int64_t)key0 * ksb + ((slot ^ (key0 & (CPR - 1) & 7)) << 4);
 #pragma unroll
         for (int u = 0; u < NS; ++u) {
             const int sc = c * NS + u;
@@ -355,7 +364,9 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                     dma16_nt(pr.kp + (int64_t)(sc * CHK + key) * ksb + ((slot ^ (key & (CPR - 1))) << 4),
                              kc[sc] + l * 1024);
                 } else {
-                    dma16_nt(ka + (int64_t)(sc * kChunk + l * KPL) * ksb, kc[sc] + l * 1024);
+                    const int key = l * KPL + key0;
+                    dma16_nt(pr.kp + (int64_t)(sc * kChunk + key) * ksb + ((slot ^ kswz<CPR>(key)) << 4),
+                             kc[sc] + l * 1024);
                 }
             }
         }
@@ -423,7 +434,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                             __builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, qf[ks]), acc, 0, 0, 0);
                     }
                 } else {
-                    const int ksw = key & (CPR - 1) & 7;
+                    const int ksw = kswz<CPR>(key);
 #pragma unroll
                     for (int kp2 = 0; kp2 < KS / 2; ++kp2) {
                         const int unit = ((D / 4) * grp) / 16 + kp2;

@@ -3,11 +3,13 @@
 // token's blocks from the score row itself).
 //
 // Scores become order-preserving unsigned keys (-0 folded onto +0; -inf and
-// NaN become key 0 = not a candidate).  The k-th largest key tau is found by a
-// radix select over the bytes of the keys (LDS histograms, see
-// kth_largest_key); keys above tau are taken, and keys equal to tau in
-// ascending block id until k are taken, so ties go to the lower id; output
-// positions come from ballot prefix counts, which keeps the ids ascending.
+// NaN become key 0 = not a candidate).  The k-th largest key tau is found bit
+// by bit from the top with ballot counts (up to 256 keys a row, see
+// kth_largest_key_bits) or by a radix select over the bytes of the keys (LDS
+// histograms, see kth_largest_key); keys above tau are taken, and keys equal
+// to tau in ascending block id until k are taken, so ties go to the lower id;
+// output positions come from ballot prefix counts, which keeps the ids
+// ascending.
 // Positions past the candidates get -1.  Integer work only: exact and
 // deterministic.
 #pragma once
@@ -71,6 +73,24 @@ __device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&key)[KPL], 
     return prefix;
 }
 
+// The k-th largest candidate key (there are more than k candidates), built
+// from the top bit down: a bit is kept when at least k keys are >= the value
+// with it set.  Ballot counts only (no LDS, no atomics, whose conflicts
+// serialise the histogram passes when the scores share their top bytes).
+template <int KPL>
+__device__ __forceinline__ uint32_t kth_largest_key_bits(const uint32_t (&key)[KPL], const int k) {
+    uint32_t prefix = 0u;
+#pragma unroll
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
+        prefix = cnt >= k ? cand : prefix;
+    }
+    return prefix;
+}
+
 // key[i] of lane l is the key of block i*64 + l (0 past MB).  emit(pos, id) is
 // called for pos in [0, k): the selected ids ascending, then -1.  hist: 256
 // ints of LDS owned by the wave.
@@ -81,7 +101,11 @@ __device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const in
 #pragma unroll
     for (int i = 0; i < KPL; ++i) ncand += __popcll(__ballot(key[i] != 0u));
     const bool take_all = ncand <= k;
-    const uint32_t tau = take_all ? 0u : kth_largest_key<KPL>(key, k, hist);
+    uint32_t tau = 0u;
+    if (!take_all) {
+        if constexpr (KPL <= 4) tau = kth_largest_key_bits<KPL>(key, k);
+        else tau = kth_largest_key<KPL>(key, k, hist);
+    }
     int above = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) above += __popcll(__ballot(key[i] > tau));
