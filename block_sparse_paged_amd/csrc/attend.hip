@@ -406,9 +406,17 @@ static int64_t token_grid(const AttnParams &p) {
     return 8 * units_per_xcd * p.splits;
 }
 
+// dynamic LDS of the token kernel: the selection row, block table and
+// first-entry tables for selections of more than 256 entries or tables of
+// more than 128 blocks (see attn_unit)
+static size_t token_xtab_bytes(const AttnParams &p) {
+    return (p.k > 256 || p.MB > 128) ? (size_t)3 * kMaxMB * sizeof(int) : 0;
+}
+
 template <int D, int KV>
 hipError_t launch_token(const AttnParams &p, hipStream_t s) {
-    hipLaunchKernelGGL((attn_token_kernel<D, KV>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((attn_token_kernel<D, KV>), dim3((unsigned)token_grid(p)), dim3(kAttnWaves * 64),
+                       token_xtab_bytes(p), s, p);
     return hipGetLastError();
 }
 

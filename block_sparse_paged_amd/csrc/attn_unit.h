@@ -220,6 +220,13 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     __shared__ int sslots[SEL ? kSelSlots : 1];
     __shared__ __attribute__((aligned(16))) int shist[SEL ? 256 : 4];
     __shared__ int slast;
+    // selection rows of more than 256 entries and block tables of more than
+    // 128 blocks (caller-made selections only): the row's entries, its block
+    // table and each block id's first entry, copied once into LDS so that
+    // resolving a page never waits on a global load while page loads fly.
+    // Dynamic LDS, given by the launch only for such sizes (token_xtab_bytes).
+    extern __shared__ int xtab[];
+    int *const lsel = xtab, *const lbt = xtab + kMaxMB, *const lfirst = xtab + 2 * kMaxMB;
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -267,6 +274,22 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     }
     const int L = clamp_len(Lraw, p.MB);
     const int vis = max(0, L - (p.T - 1 - t));
+    const int MBt = min(p.MB, kMaxMB);                // blocks the LDS table holds
+    if constexpr (!SEL) {
+        if (e1 > 256 || p.MB > 128) {                  // uniform
+            for (int i = tid; i < MBt; i += NW * 64) {
+                lbt[i] = p.bt[(int64_t)r * p.bt_sr + (int64_t)i * p.bt_sj];
+                lfirst[i] = 0x7fffffff;
+            }
+            __syncthreads();
+            for (int i = tid; i < e1; i += NW * 64) {
+                const int j = p.topk[trow + (int64_t)i * p.tk_si];
+                lsel[i] = j;
+                if (j >= 0 && j < MBt) atomicMin(&lfirst[j], i);
+            }
+            __syncthreads();
+        }
+    }
     if constexpr (SEL) {
         // wave 0 selects; the others read its slots
         if (wave == 0) select_from_values<2>(srow, p.MB, p.k, sslots, shist);
@@ -305,8 +328,9 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         for (; b < bpw; ++b) {
             const int i = e0 + pslot * bpw + b;
             if (i >= e1) break;
-            // entry i and duplicate check against entries [0, i)  (wave-uniform)
-            int j;
+            // entry i and duplicate check against entries [0, i)  (wave-uniform;
+            // with SEL, i < k <= 128)
+            int j = -1;
             bool dup = false;
             if (i < 256) {
                 const int c = i >> 6;
@@ -314,20 +338,27 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                 j = __builtin_amdgcn_readlane(src, i & 63);
 #pragma unroll
                 for (int c2 = 0; c2 < 4; ++c2) dup |= __ballot(lane + 64 * c2 < i && tkv[c2] == j) != 0;
-            } else {
-                j = p.topk[trow + (int64_t)i * p.tk_si];
-                for (int c2 = 0; c2 * 64 < i; ++c2) {
-                    const int idx = c2 * 64 + lane;
-                    const int v = (idx < i) ? p.topk[trow + (int64_t)idx * p.tk_si] : -1;
-                    dup |= __ballot(idx < i && v == j) != 0;
+            } else if constexpr (!SEL) {
+                j = lsel[i];
+                if (j >= 0 && j < MBt) {
+                    dup = lfirst[j] != i;
+                } else if (j >= MBt && j < p.MB) {
+                    // block ids past the first-entry table (tables of more than
+                    // kMaxMB blocks): compared with the earlier entries
+                    for (int c2 = 0; c2 * 64 < i; ++c2) {
+                        const int idx = c2 * 64 + lane;
+                        const int v = (idx < i) ? lsel[idx] : -1;
+                        dup |= __ballot(idx < i && v == j) != 0;
+                    }
                 }
-                __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             }
             const int kbase = j * kBlock + half * WK;
             if (dup || j < 0 || j >= p.MB || kbase >= vis) continue;
             int pid;
             if (j < 128) {
                 pid = __builtin_amdgcn_readlane(j < 64 ? btv[0] : btv[1], j & 63);
+            } else if (j < MBt) {
+                pid = lbt[j];                          // !SEL (MB <= 128 with SEL)
             } else {
                 pid = p.bt[(int64_t)r * p.bt_sr + (int64_t)j * p.bt_sj];
                 __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);

@@ -264,3 +264,35 @@ def test_tokens_that_see_few_keys(msa, kv):
     assert (excess <= 2.0 ** -14).all(), (
         f"{int((excess > 2.0 ** -14).sum())} cells off; worst at {worst}: gpu {g[worst]!r} "
         f"oracle {ref[worst]!r} (visible keys {c.visible(worst[0])})")
+
+
+def test_caller_topk_long_selection_with_gaps(msa):
+    """Selections of more than 256 entries over more than 128 blocks (the
+    token kernel resolves them from tables in LDS): -1 holes, ids >= MB,
+    duplicates of earlier entries and blocks past the visible range, all at
+    entries past 256 as well."""
+    c = synth.small_fp8(R=2, T=2, lens=(40000, 35000), k=300, seed=6601)
+    _say(f"case long selection: MB={c.MB} k={c.k}")
+    d = upload(c)
+    tk = synth.random_topk(c, seed=6602).numpy()
+    rng = np.random.default_rng(6603)
+    clean = tk.copy()
+    for n in range(c.N):
+        pos = rng.choice(np.arange(200, c.k), size=12, replace=False)
+        tk[n, pos[0]] = -1
+        tk[n, pos[1]] = c.MB + 5
+        tk[n, pos[2]] = tk[n, pos[3] - 150]                 # repeats an earlier entry
+        tk[n, pos[4]] = tk[n, 3]
+        tk[n, pos[5]] = c.MB - 1                             # may lie past the visible range
+        row = tk[n].copy()
+        row[(row >= c.MB) | (row < 0)] = -1
+        seen = set()
+        for i, j in enumerate(row):
+            if j in seen:
+                row[i] = -1
+            elif j >= 0:
+                seen.add(int(j))
+        clean[n] = row
+    out = run_attend(msa, c, d, torch.from_numpy(tk).cuda())
+    torch.cuda.synchronize()
+    check_attention(out, oracle_attention(c, clean))
