@@ -135,6 +135,37 @@ PMC_KERNELS = {"select_decode": "attn_token_select_kernel", "score": "score_mfma
 CALIB_KERNEL = "MulFunctor"          # the reference streaming kernel of --calib-copy-mib
 
 
+def short_kernel_name(name: str) -> str:
+    """A kernel's name without its return type, namespaces and argument list,
+    e.g. 'attn_token_select_kernel<128, 2>' for rocprofv3's full
+    'void msa::(anonymous namespace)::attn_token_select_kernel<128, 2>(msa::AttnParams)'."""
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):            # the trailing argument list
+        if name[i] == ")":
+            depth += 1
+        elif name[i] == "(":
+            depth -= 1
+            if depth == 0:
+                name = name[:i]
+                break
+    cut, tdepth, pdepth = 0, 0, 0
+    for i, c in enumerate(name):
+        if c == "<":
+            tdepth += 1
+        elif c == ">":
+            tdepth -= 1
+        elif c == "(":
+            pdepth += 1
+        elif c == ")":
+            pdepth -= 1
+        elif tdepth == 0 and pdepth == 0:
+            if c == " ":
+                cut = i + 1
+            elif c == ":" and name[i + 1:i + 2] == ":":
+                cut = i + 2
+    return name[cut:]
+
+
 def ktrace_summary(run_dir: str, name: str, command: str) -> None:
     """profiles/<name>_kernels.md from a rocprofv3 kernel_stats.csv, and the average
     duration of each kernel, keyed by the kernel sources' digest, into
@@ -153,10 +184,10 @@ def ktrace_summary(run_dir: str, name: str, command: str) -> None:
              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
     avg = {}
     for r in rows[:14]:
-        kname = r["Name"]
-        short = kname if len(kname) <= 90 else kname[:90]
+        short = short_kernel_name(r["Name"])
+        short = short if len(short) <= 90 else short[:90]
         a_us = float(r["AverageNs"]) / 1e3
-        avg[kname.split("(")[0]] = round(a_us, 3)
+        avg[short_kernel_name(r["Name"])] = round(a_us, 3)
         lines.append(f"| `{short}` | {r['Calls']} | {a_us:.3f} | {float(r['MinNs']) / 1e3:.3f} | "
                      f"{float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f}% |")
     with open(os.path.join(ROOT, "profiles", f"{name}_kernels.md"), "w") as fh:

@@ -52,3 +52,16 @@ def test_copies_time_the_requested_steps():
         assert s >= steps and w >= warm                   # never fewer than asked
         if any(steps % c == 0 and warm % c == 0 for c in range(5, 17)):
             assert (s, w) == (steps, warm)
+
+
+def test_short_kernel_names():
+    """The trace summary keys kernels by name without return type, namespaces
+    and argument list, whichever form rocprofv3 prints."""
+    import bench
+    full = "void msa::(anonymous namespace)::attn_token_select_kernel<128, 2>(msa::AttnParams)"
+    assert bench.short_kernel_name(full) == "attn_token_select_kernel<128, 2>"
+    assert bench.short_kernel_name("attn_token_select_kernel<128, 2>(msa::AttnParams)") == \
+        "attn_token_select_kernel<128, 2>"
+    assert bench.short_kernel_name("(anonymous namespace)::stream_read_kernel(unsigned int __vector(4) "
+                                   "const*, long, unsigned int*)") == "stream_read_kernel"
+    assert bench.short_kernel_name("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
