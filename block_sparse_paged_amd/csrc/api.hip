@@ -13,10 +13,11 @@
 using namespace msa;
 
 // Scratch of msa_decode_step_noalloc, for callers that cannot allocate: the
-// step's split partials and arrival counters (8 MiB, one array per GPU, held
-// until the process ends).  Host code never passes `scratch` itself to a
+// step's split partials and arrival counters (16 MiB, one array per GPU, held
+// until the process ends: room for every row-level plan of 16 query heads per
+// KV head, whose partials come to about 8 MiB at any batch size).  Host code never passes `scratch` itself to a
 // kernel: its device address comes from hipGetSymbolAddress (below).
-constexpr size_t kScratchBytes = (size_t)8 << 20;
+constexpr size_t kScratchBytes = (size_t)16 << 20;
 // arrival counters sit in a fixed region at its start (512 KiB, 2048 counters
 // 256 bytes apart), so that a call never finds another call's partials where
 // its counters are; every call leaves them at zero

@@ -73,7 +73,7 @@ typedef enum msa_status {
     MSA_ERR_ARG = 7,           /* a scalar argument is out of range                   */
     MSA_ERR_LAUNCH = 8,        /* the HIP runtime refused a launch                    */
     MSA_ERR_SCRATCH_LIMIT = 9, /* msa_decode_step_noalloc: sizes need more than its
-                                  8 MiB of scratch                                    */
+                                  16 MiB of scratch                                   */
     MSA_ERR_SCRATCH_SETUP = 10 /* msa_decode_step_noalloc: the scratch array's device
                                   address could not be obtained                       */
 } msa_status;
@@ -243,10 +243,10 @@ void msa_decode_step(const msa_tensor *q_idx, const msa_tensor *index_k, const m
  * harnesses that forbid allocation).  Same arguments (less the workspace),
  * domain and outputs as msa_decode_step, bit-identical to it.
  *
- * The step's scratch (split partials and arrival counters) lives in an 8 MiB
+ * The step's scratch (split partials and arrival counters) lives in a 16 MiB
  * device array inside the library, one per GPU, held until the process ends.
  * A call whose split plan needs more (with 16 query heads of dim 128: more
- * than about 900 query tokens, 8 KiB of partials each; at most 2048 query
+ * than about 1950 query tokens, 8 KiB of partials each; at most 2048 query
  * tokens x KV heads) is rejected with MSA_ERR_SCRATCH_LIMIT before anything
  * is enqueued.  The first call on a device
  * looks the array's address up and enqueues a kernel that zero-fills it on

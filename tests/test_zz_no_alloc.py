@@ -56,7 +56,8 @@ def _noalloc(msa, c, d):
 
 
 def test_noalloc_matches_workspace_step_twice(msa):
-    cases = [synth.hbm_decode(16, seed=5990),                       # 16 rows, the bench shape
+    cases = [synth.hbm_decode(128, seed=5991),                      # row-level plan, ~8 MiB of partials
+             synth.hbm_decode(16, seed=5990),                       # 16 rows, the bench shape
              synth.small_fp8(R=3, T=4, lens=(900, 5000, 130), k=6, seed=77)]   # then smaller
     for c in cases:
         _say(f"case {c.name}: R={c.R} T={c.T} k={c.k} MB={c.MB}")
@@ -76,9 +77,9 @@ def test_noalloc_matches_workspace_step_twice(msa):
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch(msa):
-    # 1024 rows x 4 tokens x 16 heads x 128 dims of split partials: > 8 MiB
+    # 1024 rows x 4 tokens x 16 heads x 128 dims of split partials: > 16 MiB
     R, T, MB, P, k = 1024, 4, 1, 4, 1
-    assert msa.msa_decode_step_workspace_bytes(R, T, 16, 1, 128, k) > (8 << 20)
+    assert msa.msa_decode_step_workspace_bytes(R, T, 16, 1, 128, k) > (16 << 20)
     f8 = torch.float8_e4m3fn
     q_idx = torch.zeros((R * T, 128), dtype=torch.bfloat16, device="cuda")
     idx = torch.zeros((P, 128, 128), dtype=torch.uint8, device="cuda").view(f8)
