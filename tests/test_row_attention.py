@@ -175,3 +175,35 @@ def test_row_attention_step_selects_in_launch(msa, D):
     assert torch.equal(topk, t1)
     assert torch.equal(out.view(torch.int16), o1.view(torch.int16))
     check_attention(out, oracle_attention(c, topk.cpu().numpy()))
+
+
+def test_row_attention_step_per_request_sheet(msa):
+    """msa_decode_step with one sheet row and one selection per request (64 of
+    each row's blocks, the selection made inside the row-level launch by one
+    wave for the whole row) equals msa_block_score -> msa_select_topk ->
+    msa_sparse_decode on the per-request sheet bit for bit, and the oracle."""
+    c = synth.make_case("row_step_per_request", R=3, T=4, Hq=16, Hkv=1, D=128, Di=128,
+                        seq_lens=[9000, 8300, 130], P=150, k=64, seed=6501)
+    _say(f"case row_step_per_request: R={c.R} T={c.T} k={c.k} MB={c.MB}")
+    d = upload(c)
+    s1 = poisoned((c.R, c.MB), torch.float32)
+    msa.msa_block_score(d.q_idx, d.index_k, d.block_table, d.seq_lens, c.T, c.B, c.idx_scale, s1)
+    t1 = poisoned((c.R, c.k), torch.int32)
+    msa.msa_select_topk(s1, c.k, t1)
+    o1 = run_attend(msa, c, d, t1)
+    scores = poisoned((c.R, c.MB), torch.float32)
+    topk = poisoned((c.R, c.k), torch.int32)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    ws = torch.zeros(msa.msa_decode_step_workspace_bytes(c.R, c.T, c.Hq, c.Hkv, c.D, c.k),
+                     dtype=torch.uint8, device="cuda")
+    msa.msa_decode_step(d.q_idx, d.index_k, d.q, d.k_cache, d.v_cache, d.block_table, d.seq_lens,
+                        c.T, c.k, c.B, c.idx_scale, c.sm_scale, c.k_scale, c.v_scale, scores, topk, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(scores.view(torch.int32), s1.view(torch.int32))
+    assert torch.equal(topk, t1)
+    assert torch.equal(out.view(torch.int16), o1.view(torch.int16))
+    gt = topk.cpu().numpy()
+    assert np.array_equal(gt, oracle.select_topk(scores.cpu().numpy().astype(np.float64), c.k))
+    ref = oracle_attention(c, gt)
+    check_attention(out, ref)
+    _near_exact(out, ref)
