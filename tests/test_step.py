@@ -126,8 +126,18 @@ def test_step_matches_oracle(msa):
     check_attention(o, oracle_attention(c, gt, threads=16))
 
 
-def test_step_repeated_and_graph_replay(msa):
-    shape = dict(R=4, T=4, lens=(3000, 16384, 9000, 128), k=16, P=300)
+GRAPH_SHAPES = {
+    # the per-token attention kernel (selection and split merge in its launch)
+    "token_k16": dict(R=4, T=4, lens=(3000, 16384, 9000, 128), k=16, P=300),
+    # the row-level attention kernel and the split merge launch (k = all blocks)
+    "row_k128": dict(R=4, T=4, lens=(9000, 16384, 8300, 128), k=128, P=300),
+}
+
+
+@pytest.mark.parametrize("name", list(GRAPH_SHAPES))
+def test_step_repeated_and_graph_replay(msa, name):
+    shape = GRAPH_SHAPES[name]
+    _say(f"case graph replay {name}")
     c0 = synth.small_fp8(seed=111, **shape)
     d = upload(c0)
     scores = poisoned((c0.N, c0.MB), torch.float32)
