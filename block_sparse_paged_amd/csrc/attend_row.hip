@@ -392,8 +392,7 @@ __global__ __launch_bounds__(kAttnWaves * 64, 1) void attn_row_kernel(AttnParams
     for (int jj = 0; jj < TPW; ++jj) {
         const int t = tok[jj];
         if (t >= NT) break;
-        float l_tot = l_run[jj] + __shfl_xor(l_run[jj], 16);
-        l_tot += __shfl_xor(l_tot, 32);
+        const float l_tot = sum_over_lane_groups(l_run[jj]);
         uint8_t *const ow = region + (t * 4 + quarter) * DT * 1024 + lane * 16;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) *(f32x4 *)(ow + dt * 1024) = o[jj][dt];

@@ -572,8 +572,7 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         have = have_n;
     }
     // full per-head sum over the wave's four lane groups
-    float l_tot = l_run + __shfl_xor(l_run, 16);
-    l_tot += __shfl_xor(l_tot, 32);
+    const float l_tot = sum_over_lane_groups(l_run);
 
     // ---- merge the 8 waves in LDS.  Wave w stores tile dt of its O^T
     // accumulator at [w][dt][lane] (16 bytes per lane: conflict-free vector

@@ -88,6 +88,27 @@ __device__ __forceinline__ int wave_prefix_sum(int x) {
     return x;
 }
 
+// Lane l's value combined with lane l ^ 16's (l ^ 32's) by gfx950's lane
+// swaps, without LDS: permlane16_swap (permlane32_swap) of a value with itself
+// returns the lane's own value and its partner's as the two results (which is
+// which depends on the lane); their sum and max are the same in both lanes.
+__device__ __forceinline__ float sum_xor16(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+
 // Sum over aligned groups of W lanes (W power of two, <= 64); every lane of a
 // group ends with the group sum.
 template <int W>
@@ -96,8 +117,8 @@ __device__ __forceinline__ float group_sum(float v) {
     if constexpr (W >= 4) v += dpp_f32<kDppXor2>(v);
     if constexpr (W >= 8) v += dpp_f32<kDppHalfMirror>(v);
     if constexpr (W >= 16) v += dpp_f32<kDppMirror>(v);
-    if constexpr (W >= 32) v += __shfl_xor(v, 16);
-    if constexpr (W >= 64) v += __shfl_xor(v, 32);
+    if constexpr (W >= 32) v = sum_xor16(v);
+    if constexpr (W >= 64) v = sum_xor32(v);
     return v;
 }
 
@@ -107,8 +128,8 @@ __device__ __forceinline__ float group_max(float v) {
     if constexpr (W >= 4) v = fmaxf(v, dpp_f32<kDppXor2>(v));
     if constexpr (W >= 8) v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
     if constexpr (W >= 16) v = fmaxf(v, dpp_f32<kDppMirror>(v));
-    if constexpr (W >= 32) v = fmaxf(v, __shfl_xor(v, 16));
-    if constexpr (W >= 64) v = fmaxf(v, __shfl_xor(v, 32));
+    if constexpr (W >= 32) v = max_xor16(v);
+    if constexpr (W >= 64) v = max_xor32(v);
     return v;
 }
 
@@ -119,23 +140,20 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
 }
 
-// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane groups), with
-// the gfx950 lane swaps: permlane32_swap of a value with itself leaves each
-// lane holding its own value and lane l ^ 32's in the two results, and
-// permlane16_swap likewise lane l ^ 16's.
-__device__ __forceinline__ float max_over_lane_groups(float v) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
+// Max over lanes l, l ^ 16, l ^ 32 and l ^ 48 (the four 16-lane groups).
+__device__ __forceinline__ float max_over_lane_groups(float v) { return max_xor16(max_xor32(v)); }
+
+// Sum over lanes l, l ^ 16, l ^ 32 and l ^ 48, the l ^ 16 pairs first.
+__device__ __forceinline__ float sum_over_lane_groups(float v) { return sum_xor32(sum_xor16(v)); }
 
 // Max over lanes whose index differs only in bits >= log2(FROM) (all lanes
 // holding equal values within groups of FROM).
 template <int FROM>
 __device__ __forceinline__ float max_across_groups(float v) {
 #pragma unroll
-    for (int off = FROM; off < 64; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    for (int off = FROM; off < 16; off <<= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if constexpr (FROM <= 16) v = max_xor16(v);
+    if constexpr (FROM <= 32) v = max_xor32(v);
     return v;
 }
 
