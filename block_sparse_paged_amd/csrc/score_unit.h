@@ -46,6 +46,7 @@ __device__ __forceinline__ void score_page(const ScoreParams &p, const int r, co
     }
     const int L = clamp_len(Lraw, p.MB);
     const int vmax = max(0, L);                 // the row's last token sees L keys
+    const int vmin = max(0, L - (p.T - 1));     // and its first L - (T - 1)
     const int vt = tok ? max(0, L - (p.T - 1 - li)) : 0;
     float best = -INFINITY;
     bool bad_page = false;
@@ -60,10 +61,12 @@ __device__ __forceinline__ void score_page(const ScoreParams &p, const int r, co
 #pragma unroll
                 for (int h = 0; h < NL; ++h)
                     kf[kt][h] = load_nt16(pg + (int64_t)(kt * 16 + li) * p.k_sb + LB * grp + 16 * h);
-            const int kbase = j * kBlock;
+            // eight independent accumulators (one per 16-key tile), so that no
+            // tile waits for the previous tile's products before its own
+            f32x4 acc[8];
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                acc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
                     const uint4 raw = kf[kt][ks >> 1];
@@ -71,21 +74,32 @@ __device__ __forceinline__ void score_page(const ScoreParams &p, const int r, co
                     uint4 a;
                     a.x = fp8x2_to_bf16x2<false>(lo); a.y = fp8x2_to_bf16x2<true>(lo);
                     a.z = fp8x2_to_bf16x2<false>(hi); a.w = fp8x2_to_bf16x2<true>(hi);
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                  __builtin_bit_cast(bf16x8, qf[ks]), acc, 0, 0, 0);
+                    acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                      __builtin_bit_cast(bf16x8, qf[ks]), acc[kt],
+                                                                      0, 0, 0);
                 }
-                // acc[e] = dot of key 16*kt + 4*grp + e with token li
-                if (kbase + kBlock <= vt) {                 // whole page visible to this token
-                    best = fmaxf(best, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
-                } else {
+            }
+            // acc[kt][e] = dot of key 16*kt + 4*grp + e with token li
+            const int kbase = j * kBlock;
+            if (kbase + kBlock <= vmin) {
+                // the whole page is visible to every token of the row (one
+                // branch for the wave); the products of a visible key are dot
+                // products of finite codes (a NaN code there is outside the
+                // contract), so the maximum needs no NaN quieting
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+                    best = max3f(best, max3f(acc[kt][0], acc[kt][1], acc[kt][2]), acc[kt][3]);
+            } else {
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int pos = kbase + kt * 16 + 4 * grp + e;
-                        best = (pos < vt) ? fmaxf(best, acc[e]) : best;
+                        best = (pos < vt) ? fmaxf(best, acc[kt][e]) : best;
                     }
-                }
             }
             best = max_across_groups<16>(best);
+            if (!tok) best = -INFINITY;                 // unused columns
         }
     }
     if (p.per_row) {
