@@ -336,8 +336,11 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
                 const int c = i >> 6;
                 const int src = c == 0 ? tkv[0] : c == 1 ? tkv[1] : c == 2 ? tkv[2] : tkv[3];
                 j = __builtin_amdgcn_readlane(src, i & 63);
+                // a selection made here is a set of distinct ids
+                if constexpr (!SEL) {
 #pragma unroll
-                for (int c2 = 0; c2 < 4; ++c2) dup |= __ballot(lane + 64 * c2 < i && tkv[c2] == j) != 0;
+                    for (int c2 = 0; c2 < 4; ++c2) dup |= __ballot(lane + 64 * c2 < i && tkv[c2] == j) != 0;
+                }
             } else if constexpr (!SEL) {
                 j = lsel[i];
                 if (j >= 0 && j < MBt) {

@@ -3,11 +3,12 @@
 // token's blocks from the score row itself).
 //
 // Scores become order-preserving unsigned keys (-0 folded onto +0; -inf and
-// NaN become key 0 = not a candidate).  The k-th largest key tau is found bit
-// by bit from the top with ballot counts (up to 256 keys a row, see
-// kth_largest_key_bits) or by a radix select over the bytes of the keys (LDS
-// histograms, see kth_largest_key); keys above tau are taken, and keys equal
-// to tau in ascending block id until k are taken, so ties go to the lower id;
+// NaN become key 0 = not a candidate).  A threshold tau -- the k-th largest
+// key, or a value that exactly k keys reach -- is found bit by bit from the
+// top with ballot counts (up to 256 keys a row, see kth_largest_key_bits) or
+// by a radix select over the bytes of the keys (LDS histograms, see
+// kth_largest_key); keys above tau are taken, and keys equal to tau in
+// ascending block id until k are taken, so ties go to the lower id;
 // output positions come from ballot prefix counts, which keeps the ids
 // ascending.
 // Positions past the candidates get -1.  Integer work only: exact and
@@ -73,20 +74,90 @@ __device__ __forceinline__ uint32_t kth_largest_key(const uint32_t (&key)[KPL], 
     return prefix;
 }
 
-// The k-th largest candidate key (there are more than k candidates), built
-// from the top bit down: a bit is kept when at least k keys are >= the value
-// with it set.  Ballot counts only (no LDS, no atomics, whose conflicts
-// serialise the histogram passes when the scores share their top bytes).
+// One step of the bitwise search below: candidate c = prefix | bit, n = the
+// number of keys >= c; c is kept (prefix = c, cnt = n) when n >= k.  Written
+// as one block of assembly so that the KPL compares go into SGPR pairs of
+// their own and issue back to back, and the scalar counts wait for them once
+// (compiled from C, every compare and count went through the same pair, two
+// vector-to-scalar waits a step).  KPL is 1, 2 or 4.
+template <int KPL>
+__device__ __forceinline__ void kth_bit_step(uint32_t &prefix, int &cnt, const uint32_t bit,
+                                             const uint32_t (&key)[KPL], const int k) {
+    uint32_t c, n, t1, t2, t3;
+    uint64_t m0, m1, m2, m3;
+    if constexpr (KPL == 1) {
+        asm volatile(
+            "s_or_b32 %[c], %[p], %[b]\n\t"
+            "v_cmp_le_u32_e64 %[m0], %[c], %[k0]\n\t"
+            "s_bcnt1_i32_b64 %[n], %[m0]\n\t"
+            "s_cmp_ge_u32 %[n], %[k]\n\t"
+            "s_cselect_b32 %[p], %[c], %[p]\n\t"
+            "s_cselect_b32 %[cnt], %[n], %[cnt]"
+            : [p] "+s"(prefix), [cnt] "+s"(cnt), [c] "=&s"(c), [n] "=&s"(n), [m0] "=&s"(m0)
+            : [b] "s"(bit), [k0] "v"(key[0]), [k] "s"(k)
+            : "scc");
+    } else if constexpr (KPL == 2) {
+        asm volatile(
+            "s_or_b32 %[c], %[p], %[b]\n\t"
+            "v_cmp_le_u32_e64 %[m0], %[c], %[k0]\n\t"
+            "v_cmp_le_u32_e64 %[m1], %[c], %[k1]\n\t"
+            "s_bcnt1_i32_b64 %[n], %[m0]\n\t"
+            "s_bcnt1_i32_b64 %[t1], %[m1]\n\t"
+            "s_add_u32 %[n], %[n], %[t1]\n\t"
+            "s_cmp_ge_u32 %[n], %[k]\n\t"
+            "s_cselect_b32 %[p], %[c], %[p]\n\t"
+            "s_cselect_b32 %[cnt], %[n], %[cnt]"
+            : [p] "+s"(prefix), [cnt] "+s"(cnt), [c] "=&s"(c), [n] "=&s"(n), [t1] "=&s"(t1), [m0] "=&s"(m0),
+              [m1] "=&s"(m1)
+            : [b] "s"(bit), [k0] "v"(key[0]), [k1] "v"(key[1]), [k] "s"(k)
+            : "scc");
+    } else {
+        static_assert(KPL == 4, "KPL 1, 2 or 4");
+        asm volatile(
+            "s_or_b32 %[c], %[p], %[b]\n\t"
+            "v_cmp_le_u32_e64 %[m0], %[c], %[k0]\n\t"
+            "v_cmp_le_u32_e64 %[m1], %[c], %[k1]\n\t"
+            "v_cmp_le_u32_e64 %[m2], %[c], %[k2]\n\t"
+            "v_cmp_le_u32_e64 %[m3], %[c], %[k3]\n\t"
+            "s_bcnt1_i32_b64 %[n], %[m0]\n\t"
+            "s_bcnt1_i32_b64 %[t1], %[m1]\n\t"
+            "s_bcnt1_i32_b64 %[t2], %[m2]\n\t"
+            "s_bcnt1_i32_b64 %[t3], %[m3]\n\t"
+            "s_add_u32 %[n], %[n], %[t1]\n\t"
+            "s_add_u32 %[t2], %[t2], %[t3]\n\t"
+            "s_add_u32 %[n], %[n], %[t2]\n\t"
+            "s_cmp_ge_u32 %[n], %[k]\n\t"
+            "s_cselect_b32 %[p], %[c], %[p]\n\t"
+            "s_cselect_b32 %[cnt], %[n], %[cnt]"
+            : [p] "+s"(prefix), [cnt] "+s"(cnt), [c] "=&s"(c), [n] "=&s"(n), [t1] "=&s"(t1), [t2] "=&s"(t2),
+              [t3] "=&s"(t3), [m0] "=&s"(m0), [m1] "=&s"(m1), [m2] "=&s"(m2), [m3] "=&s"(m3)
+            : [b] "s"(bit), [k0] "v"(key[0]), [k1] "v"(key[1]), [k2] "v"(key[2]), [k3] "v"(key[3]), [k] "s"(k)
+            : "scc");
+    }
+}
+
+// The threshold of the k largest candidate keys (there are more than k
+// candidates), built from the top bit down: a bit is kept when at least k keys
+// are >= the value with it set.  Ballot counts only (no LDS, no atomics,
+// whose conflicts serialise the histogram passes when the scores share their
+// top bytes).  The search stops as soon as exactly k keys are >= the value
+// built so far (the k-th and (k+1)-th largest keys first differ in the last
+// bit kept): the value returned then has the remaining bits zero, and exactly
+// k keys are >= it; otherwise it is the k-th largest key.  Selection from it
+// (keys above it, then keys equal to it by ascending id) is the same either
+// way.
 template <int KPL>
 __device__ __forceinline__ uint32_t kth_largest_key_bits(const uint32_t (&key)[KPL], const int k) {
+    constexpr int KP = KPL <= 1 ? 1 : KPL <= 2 ? 2 : 4;     // registers searched (padding keys are 0)
+    uint32_t kp[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) kp[i] = i < KPL ? key[i] : 0u;
     uint32_t prefix = 0u;
+    int cnt = 64 * KP;                               // keys >= 0; more than k
 #pragma unroll
     for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = prefix | (1u << b);
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) cnt += __popcll(__ballot(key[i] >= cand));
-        prefix = cnt >= k ? cand : prefix;
+        kth_bit_step<KP>(prefix, cnt, 1u << b, kp, k);
+        if (cnt == k) break;
     }
     return prefix;
 }
