@@ -162,12 +162,14 @@ __device__ __forceinline__ uint32_t kth_largest_key_bits(const uint32_t (&key)[K
     return prefix;
 }
 
-// key[i] of lane l is the key of block i*64 + l (0 past MB).  emit(pos, id) is
-// called for pos in [0, k): the selected ids ascending, then -1.  hist: 256
-// ints of LDS owned by the wave.
-template <int KPL, class Emit>
-__device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const int k, int *hist, Emit emit) {
-    const int lane = threadIdx.x & 63;
+// The selection of a row as lane masks: key[i] of lane l is the key of block
+// i*64 + l (0 past MB); bit l of selm[i] is set when that block is selected.
+// The selected ids, ascending, are the set bits in order of (i, lane); there
+// are min(k, candidates) of them.  hist: 256 ints of LDS owned by the wave
+// (used only for KPL > 4).
+template <int KPL>
+__device__ __forceinline__ void select_masks(const uint32_t (&key)[KPL], const int k, int *hist,
+                                             uint64_t (&selm)[KPL]) {
     int ncand = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) ncand += __popcll(__ballot(key[i] != 0u));
@@ -181,7 +183,7 @@ __device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const in
 #pragma unroll
     for (int i = 0; i < KPL; ++i) above += __popcll(__ballot(key[i] > tau));
     const int need = k - above;                          // keys equal to tau to take
-    int eq_base = 0, out_base = 0;
+    int eq_base = 0;
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const uint64_t eq = __ballot(!take_all && key[i] == tau && key[i] != 0u);
@@ -189,11 +191,32 @@ __device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const in
         eq_base += __popcll(eq);
         const bool sel = take_all ? key[i] != 0u
                                   : (key[i] > tau || (key[i] == tau && eq_rank < need));
-        const uint64_t sm = __ballot(sel);
-        if (sel) emit(out_base + lanes_below(sm), i * 64 + lane);
+        selm[i] = __ballot(sel);
+    }
+}
+
+// emit(pos, id) for pos in [0, k): the ids of the masks ascending, then -1.
+template <int KPL, class Emit>
+__device__ __forceinline__ void emit_selection(const uint64_t (&selm)[KPL], const int k, Emit emit) {
+    const int lane = threadIdx.x & 63;
+    int out_base = 0;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const uint64_t sm = selm[i];
+        if ((sm >> lane) & 1u) emit(out_base + lanes_below(sm), i * 64 + lane);
         out_base += __popcll(sm);
     }
     for (int q = out_base + lane; q < k; q += 64) emit(q, -1);
+}
+
+// key[i] of lane l is the key of block i*64 + l (0 past MB).  emit(pos, id) is
+// called for pos in [0, k): the selected ids ascending, then -1.  hist: 256
+// ints of LDS owned by the wave.
+template <int KPL, class Emit>
+__device__ __forceinline__ void select_keys(const uint32_t (&key)[KPL], const int k, int *hist, Emit emit) {
+    uint64_t selm[KPL];
+    select_masks<KPL>(key, k, hist, selm);
+    emit_selection<KPL>(selm, k, emit);
 }
 
 // Score row n of the sheet -> topk row n.
