@@ -671,25 +671,36 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     if (!slast) return;
     if (active) {
         // every split wrote (m, l, acc) (m = -inf, l = 0, acc = 0 when empty):
-        // load them all at once, weight with selects, sum in split order
+        // all S <= kTokenMaxSplits of them are requested at once (one memory
+        // round trip, not one per few splits), then weighted and summed in
+        // split order
+        static_assert(kTokenMaxSplits % 4 == 0, "partials named four at a time");
         const int S = p.splits;
+        f32x4 as[kTokenMaxSplits];
+        f32x2 ml[kTokenMaxSplits];
+#pragma unroll
+        for (int u = 0; u < kTokenMaxSplits; ++u) {
+            if (u < S) {
+                as[u] = ld_coherent4_nowait(p.part_acc + part_acc_index(u, n, h, d0, N, p.Hq, D));
+                ml[u] = ld_coherent2(p.part_ml + part_ml_index(u, n, h, N, p.Hq));
+            } else {
+                as[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                ml[u] = f32x2{-INFINITY, 0.f};
+            }
+        }
+        // one wait for all of them; the empty statements after it (kept in
+        // order) name the loaded registers, so that no use of them is
+        // scheduled before the wait
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int u = 0; u < kTokenMaxSplits; u += 4)
+            asm volatile("" : "+v"(as[u]), "+v"(as[u + 1]), "+v"(as[u + 2]), "+v"(as[u + 3])::"memory");
         float m2 = -INFINITY, l2 = 0.f;
         f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
-        for (int s0 = 0; s0 < S; s0 += 4) {
-            f32x2 ml[4];
-            f32x4 as[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int sp = min(s0 + u, S - 1);
-                as[u] = ld_coherent4_nowait(p.part_acc + part_acc_index(sp, n, h, d0, N, p.Hq, D));
-                ml[u] = ld_coherent2(p.part_ml + part_ml_index(sp, n, h, N, p.Hq));
-            }
-            // the wait names the loaded registers, so that no use of them is
-            // scheduled before it
-            asm volatile("s_waitcnt vmcnt(0)" : "+v"(as[0]), "+v"(as[1]), "+v"(as[2]), "+v"(as[3])::"memory");
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float mu = (s0 + u < S) ? ml[u].x : -INFINITY;
+        for (int u = 0; u < kTokenMaxSplits; ++u) {
+            if (u < S) {
+                const float mu = ml[u].x;
                 const float mn = fmaxf(m2, mu);
                 const float wo = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
                 const float wn = (mu == -INFINITY) ? 0.f : exp2_fast(mu - mn);

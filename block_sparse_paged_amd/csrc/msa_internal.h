@@ -10,7 +10,7 @@ constexpr int kBlock = 128;          // tokens per page (vLLM design note: block
 constexpr int kMaxMB = 2048;         // logical blocks per row served by select/attention
 constexpr int kTokGroup = 4;         // query tokens of one row handled together
 constexpr int kSplitTargetWGs = 256; // attention workgroups aimed for (one per CU)
-constexpr int kTokenMaxSplits = 16;  // splits of one token's selection list (MFMA path)
+constexpr int kTokenMaxSplits = 8;   // splits of one token's selection list (MFMA path)
 constexpr int kCounterStride = 64;   // int32s between split-arrival counters (one per 256 B)
 constexpr int kRowMaxSplits = 32;    // splits of one row's block list (row-level attention)
 
