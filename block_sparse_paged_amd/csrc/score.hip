@@ -194,9 +194,9 @@ __global__ __launch_bounds__(256) void score_valu_kernel(ScoreParams p) {
 
 // pages (one per wave) per workgroup: 4, or 1 when the batch has too few
 // pages to give every CU a workgroup of 4
-template <int DI>
+template <int DI, bool STAGE>
 __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int WPG = blockDim.x >> 6;
     const int JC = (p.MB + WPG - 1) / WPG;
     int r, jc;
@@ -214,7 +214,9 @@ __global__ __launch_bounds__(256) void score_mfma_decode_kernel(ScoreParams p) {
     }
     const int j = jc * WPG + wave;
     if (j >= p.MB) return;                      // no barriers in this kernel
-    score_page<DI>(p, r, j);
+    // STAGE: 128 * DI bytes of LDS per wave (dynamic: WPG waves)
+    extern __shared__ __attribute__((aligned(16))) uint8_t spages[];
+    score_page<DI, STAGE>(p, r, j, spages + wave * (kBlock * DI));
 }
 
 // ------------------------------------------------------------------ MFMA path
@@ -299,7 +301,12 @@ hipError_t launch_mfma_decode(const ScoreParams &p, hipStream_t s) {
     const int64_t JC = (p.MB + WPG - 1) / WPG;
     // R >= 8: 8 XCDs x ceil(R / 8) rows each x JC (see the kernel)
     const int64_t grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * JC : (int64_t)p.R * JC;
-    hipLaunchKernelGGL((score_mfma_decode_kernel<DI>), dim3((unsigned)grid), dim3(64 * WPG), 0, s, p);
+    // pages staged through LDS when the launch has at least two waves per CU
+    if (grid * WPG >= 2 * kSplitTargetWGs)
+        hipLaunchKernelGGL((score_mfma_decode_kernel<DI, true>), dim3((unsigned)grid), dim3(64 * WPG),
+                           (size_t)WPG * kBlock * DI, s, p);
+    else
+        hipLaunchKernelGGL((score_mfma_decode_kernel<DI, false>), dim3((unsigned)grid), dim3(64 * WPG), 0, s, p);
     return hipGetLastError();
 }
 
