@@ -383,20 +383,20 @@ def _code_pages(n_pages: int, Di: int, first: int = 0) -> torch.Tensor:
 
 
 def fp8_code_score_case(Di: int = 128, T: int = 4, q_f32: bool = False, idx_scale: float = 1.0,
-                        seed: int = 6100) -> Case:
-    """Block scores over pages of constant codes: 2 rows x 128 blocks, page
-    (r, j) holding finite code number 128 r + j (mod 254), so every finite code
-    is some page; row 1 ends 5 keys into its last block, whose remaining keys
-    hold the two NaN codes.  Token n's query is one-hot (1.0) at dimension
-    (7 n + 3) mod Di, so its score for block j is the value of page j's code
-    times idx_scale."""
-    R, MB = 2, 128
+                        seed: int = 6100, R: int = 2) -> Case:
+    """Block scores over pages of constant codes: R >= 2 rows x 128 blocks,
+    page (r, j) holding finite code number 128 r + j (mod 254), so every finite
+    code is some page; row 1 ends 5 keys into its last block, whose remaining
+    keys hold the two NaN codes, the other rows are whole.  Token n's query is
+    one-hot (1.0) at dimension (7 n + 3) mod Di, so its score for block j is
+    the value of page j's code times idx_scale."""
+    MB = 128
     P = R * MB + 1
     perm = _rng(seed, "perm").permutation(P).astype(np.int32)
     bt = perm[:R * MB].reshape(R, MB).copy()
     index_k = torch.full((P, BLOCK, Di), E4M3_NAN_CODE, dtype=torch.uint8)
     index_k[torch.from_numpy(bt.reshape(-1).astype(np.int64))] = _code_pages(R * MB, Di)
-    lens = [MB * BLOCK, (MB - 1) * BLOCK + 5]
+    lens = [MB * BLOCK, (MB - 1) * BLOCK + 5] + [MB * BLOCK] * (R - 2)
     last = int(bt[1, MB - 1])
     index_k[last, 5::2] = 0x7F
     index_k[last, 6::2] = 0xFF
@@ -405,7 +405,7 @@ def fp8_code_score_case(Di: int = 128, T: int = 4, q_f32: bool = False, idx_scal
     for n in range(N):
         qi[n, (7 * n + 3) % Di] = 1.0
     q_idx = torch.from_numpy(qi) if q_f32 else to_bf16(qi)
-    return Case(name=f"fp8_codes_score_di{Di}_t{T}", R=R, T=T, Hq=16, Hkv=1, D=128, Di=Di, P=P,
+    return Case(name=f"fp8_codes_score_di{Di}_t{T}_r{R}", R=R, T=T, Hq=16, Hkv=1, D=128, Di=Di, P=P,
                 MB=MB, k=16, B=BLOCK, fp8=True, seq_lens=torch.tensor(lens, dtype=torch.int32),
                 block_table=torch.from_numpy(bt), q_idx=q_idx, index_k=index_k, q=None,
                 k_cache=None, v_cache=None, idx_scale=float(np.float32(idx_scale)), k_scale=1.0,

@@ -5,8 +5,9 @@ through the ATOM kernel library", "Supported experiment").
 Every finite code is placed where the result is that code's value alone, so
 the GPU must equal the oracle exactly (fp32 holds every product involved):
   * block scores over pages of constant codes with one-hot queries: the MFMA
-    decode score kernel, the vector score kernel (bf16 and fp32 queries), the
-    prefill score sheet, with idx_scale 1 and a scale that rounds;
+    decode score kernel (pages loaded straight into registers, and staged
+    through LDS), the vector score kernel (bf16 and fp32 queries), the prefill
+    score sheet, with idx_scale 1 and a scale that rounds;
   * the ragged prefill score-to-selection call over the same pages, whose
     selections order every prefix of the codes from the top and the bottom;
   * attention with one visible key (out = v_scale * value(V code)) on the MFMA
@@ -41,6 +42,10 @@ def _say(msg):
 SCORE_CASES = {
     "mfma_decode_di128": dict(Di=128, T=4),
     "mfma_decode_di64_t16": dict(Di=64, T=16),
+    # 8 rows: 1024 waves, pages staged through LDS (fewer rows load straight
+    # into registers)
+    "mfma_decode_di128_staged": dict(Di=128, T=4, R=8),
+    "mfma_decode_di64_t16_staged": dict(Di=64, T=16, R=8),
     "vector_bf16q_di32": dict(Di=32, T=4),
     "vector_f32q_di128": dict(Di=128, T=3, q_f32=True),
     "prefill_sheet_t40": dict(Di=128, T=40),
