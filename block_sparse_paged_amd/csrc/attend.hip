@@ -460,8 +460,10 @@ static int union_splits(int32_t R, int32_t T, int32_t Hkv, int32_t k) {
 // KV head) unit, at most kTokenMaxSplits (the last workgroup of a unit merges
 // all S partials).  A slot streams its pages back to back, so one round of
 // workgroups with several pages per slot costs less than several rounds; a
-// small batch takes fewer than 4 entries per split (down to one page per
-// workgroup) so that its few units still spread over many CUs.
+// small batch takes fewer than 4 entries per split (down to two pages per
+// workgroup at the cap of 8 splits: more splits would leave each token's last
+// workgroup taking in more partials than it streams pages) so that its few
+// units still spread over many CUs.
 static void token_split(int64_t units, int32_t k, int32_t *S, int32_t *bpw, int32_t *epw) {
     int64_t s = units > 0 ? (kSplitTargetWGs + units - 1) / units : 1;
     s = s > k ? k : s;
