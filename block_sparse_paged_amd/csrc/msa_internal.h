@@ -9,7 +9,8 @@ namespace msa {
 constexpr int kBlock = 128;          // tokens per page (vLLM design note: block size 128)
 constexpr int kMaxMB = 2048;         // logical blocks per row served by select/attention
 constexpr int kTokGroup = 4;         // query tokens of one row handled together
-constexpr int kSplitTargetWGs = 256; // attention workgroups aimed for (one per CU)
+constexpr int kChipCUs = 256;        // compute units of an MI355X (8 XCDs of 32)
+constexpr int kSplitTargetWGs = kChipCUs;  // attention workgroups aimed for (one per CU)
 constexpr int kTokenMaxSplits = 8;   // splits of one token's selection list (MFMA path)
 constexpr int kCounterStride = 64;   // int32s between split-arrival counters (one per 256 B)
 constexpr int kRowMaxSplits = 32;    // splits of one row's block list (row-level attention)

@@ -302,7 +302,7 @@ hipError_t launch_mfma_decode(const ScoreParams &p, hipStream_t s) {
     // R >= 8: 8 XCDs x ceil(R / 8) rows each x JC (see the kernel)
     const int64_t grid = p.R >= 8 ? 8 * ((p.R + 7) / 8) * JC : (int64_t)p.R * JC;
     // pages staged through LDS when the launch has at least two waves per CU
-    if (grid * WPG >= 2 * kSplitTargetWGs)
+    if (grid * WPG >= 2 * kChipCUs)
         hipLaunchKernelGGL((score_mfma_decode_kernel<DI, true>), dim3((unsigned)grid), dim3(64 * WPG),
                            (size_t)WPG * kBlock * DI, s, p);
     else
