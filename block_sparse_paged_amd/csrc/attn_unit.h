@@ -83,18 +83,8 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Device-coherent accesses (agent scope: sc1 loads and stores, no
-// cache-maintenance fences) for the in-launch split hand-off.  The 16-byte
-// forms are inline assembly: a load's result may only be used after an
-// explicit vmcnt wait that names the result register.
-__device__ __forceinline__ void st_coherent4(float *p, f32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
-}
-__device__ __forceinline__ f32x4 ld_coherent4_nowait(const float *p) {
-    f32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
+// Device-coherent 8-byte accesses (agent scope: sc1 loads and stores, no
+// cache-maintenance fences) for the in-launch split hand-off.
 __device__ __forceinline__ void st_coherent2(float *p, float a, float b) {
     const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
     __hip_atomic_store((uint64_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -651,14 +641,26 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         return;
     }
     float *const ml_dst = p.part_ml + part_ml_index(qs, n, h, N, p.Hq);
-    float *const acc_dst = p.part_acc + part_acc_index(qs, n, h, d0, N, p.Hq, D);
+    // A split's partial: (m, l) in fp32 and its accumulator divided by l -- a
+    // weighted average of V rows, |x| <= max |V| -- as fp16 (round to nearest,
+    // 2^-12 relative; the merged output is a convex combination of the
+    // averages, so its error stays below 2^-12 max |V|, under its own bf16
+    // rounding), four per thread in the fp32 layout's element order at half
+    // its offsets: half the bytes written and read back.
+    uint64_t *const acc_dst = (uint64_t *)p.part_acc + part_acc_index(qs, n, h, d0, N, p.Hq, D) / 4;
     // Split hand-off.  Partials are written and read with device-coherent
     // (sc1) accesses and the arrival counter is a device-scope atomic, so the
     // workgroups of one token may sit on different XCDs; no fence (which would
     // write back and invalidate the whole L2) is needed: each writer waits for
     // its stores to complete before the workgroup's single counter increment.
     store_topk();
-    if (active) st_coherent4(acc_dst, acc4);
+    if (active) {
+        const f32x4 avg = acc4 * (lm > 0.f ? 1.f / lm : 0.f);
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+        const h2 lo = {(_Float16)avg[0], (_Float16)avg[1]}, hi = {(_Float16)avg[2], (_Float16)avg[3]};
+        const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+        __hip_atomic_store(acc_dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
     if (wave == 0 && grp == 0) st_coherent2(ml_dst, mx, lm);
     wait_vmcnt<0>();
     __syncthreads();
@@ -670,42 +672,38 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     __syncthreads();
     if (!slast) return;
     if (active) {
-        // every split wrote (m, l, acc) (m = -inf, l = 0, acc = 0 when empty):
-        // all S <= kTokenMaxSplits of them are requested at once (one memory
-        // round trip, not one per few splits), then weighted and summed in
-        // split order
-        static_assert(kTokenMaxSplits % 4 == 0, "partials named four at a time");
+        // every split wrote (m, l, average) (m = -inf, l = 0, average = 0
+        // when empty): all S <= kTokenMaxSplits of them are requested before
+        // the first is used (one memory round trip, not one per split), then
+        // weighted and summed in split order
         const int S = p.splits;
-        f32x4 as[kTokenMaxSplits];
+        uint64_t av[kTokenMaxSplits];
         f32x2 ml[kTokenMaxSplits];
 #pragma unroll
         for (int u = 0; u < kTokenMaxSplits; ++u) {
             if (u < S) {
-                as[u] = ld_coherent4_nowait(p.part_acc + part_acc_index(u, n, h, d0, N, p.Hq, D));
+                av[u] = __hip_atomic_load((const uint64_t *)p.part_acc + part_acc_index(u, n, h, d0, N, p.Hq, D) / 4,
+                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 ml[u] = ld_coherent2(p.part_ml + part_ml_index(u, n, h, N, p.Hq));
             } else {
-                as[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+                av[u] = 0;
                 ml[u] = f32x2{-INFINITY, 0.f};
             }
         }
-        // one wait for all of them; the empty statements after it (kept in
-        // order) name the loaded registers, so that no use of them is
-        // scheduled before the wait
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int u = 0; u < kTokenMaxSplits; u += 4)
-            asm volatile("" : "+v"(as[u]), "+v"(as[u + 1]), "+v"(as[u + 2]), "+v"(as[u + 3])::"memory");
         float m2 = -INFINITY, l2 = 0.f;
         f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < kTokenMaxSplits; ++u) {
             if (u < S) {
+                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                const h2 lo = __builtin_bit_cast(h2, (uint32_t)av[u]), hi = __builtin_bit_cast(h2, (uint32_t)(av[u] >> 32));
+                const f32x4 avg = {(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
                 const float mu = ml[u].x;
                 const float mn = fmaxf(m2, mu);
                 const float wo = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
                 const float wn = (mu == -INFINITY) ? 0.f : exp2_fast(mu - mn);
                 l2 = l2 * wo + ml[u].y * wn;
-                a2 = a2 * wo + as[u] * wn;
+                a2 = a2 * wo + avg * (ml[u].y * wn);
                 m2 = mn;
             }
         }

@@ -116,6 +116,9 @@ hipError_t launch_prefill_select(const PrefillSelParams &p, int Di, hipStream_t 
 // contiguous:
 //   (m, l)       at part_ml[part_ml_index(s, n, h)]     (2 floats)
 //   acc[d]       at part_acc[part_acc_index(s, n, h, d)]
+// (the per-token MFMA unit, which merges its splits itself, leaves acc / l
+// instead, as fp16 at the same element positions of a half-size array:
+// ((_Float16 *)part_acc)[part_acc_index(s, n, h, d)])
 __host__ __device__ __forceinline__ int64_t part_ml_index(int s, int64_t n, int h, int64_t N, int Hq) {
     return (((int64_t)s * N + n) * Hq + h) * 2;
 }
