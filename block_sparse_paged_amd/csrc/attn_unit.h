@@ -83,8 +83,35 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Device-coherent 8-byte accesses (agent scope: sc1 loads and stores, no
-// cache-maintenance fences) for the in-launch split hand-off.
+// Device-coherent accesses (agent scope: sc1 loads and stores, no
+// cache-maintenance fences) for the in-launch split hand-off.  The 12-byte
+// forms are inline assembly: a load's result may only be used after an
+// explicit vmcnt wait that names the result register.
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+__device__ __forceinline__ void st_coherent12(uint32_t *p, u32x3 v) {
+    asm volatile("global_store_dwordx3 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
+__device__ __forceinline__ u32x3 ld_coherent12_nowait(const uint32_t *p) {
+    u32x3 v;
+    asm volatile("global_load_dwordx3 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+    return v;
+}
+
+// Four fp32 values as four 24-bit floats (sign, 8-bit exponent, 15-bit
+// mantissa: fp32 rounded to nearest even on its low 8 bits, 2^-16 relative)
+// packed into three words, and back.  Finite inputs only.
+__device__ __forceinline__ uint32_t f32_to_f24(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u + 0x7fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ u32x3 pack_f24x4(f32x4 v) {
+    const uint32_t a = f32_to_f24(v[0]), b = f32_to_f24(v[1]), c = f32_to_f24(v[2]), d = f32_to_f24(v[3]);
+    return u32x3{a | (b << 24), (b >> 8) | (c << 16), (c >> 16) | (d << 8)};
+}
+__device__ __forceinline__ f32x4 unpack_f24x4(u32x3 w) {
+    return f32x4{__uint_as_float(w.x << 8), __uint_as_float((w.x >> 24 | w.y << 8) << 8),
+                 __uint_as_float((w.y >> 16 | w.z << 16) << 8), __uint_as_float(w.z & 0xffffff00u)};
+}
 __device__ __forceinline__ void st_coherent2(float *p, float a, float b) {
     const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
     __hip_atomic_store((uint64_t *)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -641,26 +668,22 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
         return;
     }
     float *const ml_dst = p.part_ml + part_ml_index(qs, n, h, N, p.Hq);
-    // A split's partial: (m, l) in fp32 and its accumulator divided by l -- a
-    // weighted average of V rows, |x| <= max |V| -- as fp16 (round to nearest,
-    // 2^-12 relative; the merged output is a convex combination of the
-    // averages, so its error stays below 2^-12 max |V|, under its own bf16
-    // rounding), four per thread in the fp32 layout's element order at half
-    // its offsets: half the bytes written and read back.
-    uint64_t *const acc_dst = (uint64_t *)p.part_acc + part_acc_index(qs, n, h, d0, N, p.Hq, D) / 4;
+    // A split's partial: (m, l) in fp32 and its accumulator as 24-bit floats
+    // (fp32 rounded to 15 mantissa bits, 2^-16 relative: the merged output is
+    // off by at most 2^-16 of the largest V, far inside its own bf16
+    // rounding), four per thread in three words at 3/4 of the fp32 layout's
+    // offsets: a quarter fewer bytes written and read back.  (fp16 averages,
+    // half the bytes, were measured 0.3 us faster per step but leave up to
+    // 2^-11 of the largest V where splits cancel; 16-bit fixed point over
+    // the E4M3 range missed near-zero outputs by up to 2^-7 codes.)
+    const int64_t acc_i = part_acc_index(qs, n, h, d0, N, p.Hq, D);
     // Split hand-off.  Partials are written and read with device-coherent
     // (sc1) accesses and the arrival counter is a device-scope atomic, so the
     // workgroups of one token may sit on different XCDs; no fence (which would
     // write back and invalidate the whole L2) is needed: each writer waits for
     // its stores to complete before the workgroup's single counter increment.
     store_topk();
-    if (active) {
-        const f32x4 avg = acc4 * (lm > 0.f ? 1.f / lm : 0.f);
-        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-        const h2 lo = {(_Float16)avg[0], (_Float16)avg[1]}, hi = {(_Float16)avg[2], (_Float16)avg[3]};
-        const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, lo) | ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
-        __hip_atomic_store(acc_dst, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (active) st_coherent12((uint32_t *)p.part_acc + acc_i / 4 * 3, pack_f24x4(acc4));
     if (wave == 0 && grp == 0) st_coherent2(ml_dst, mx, lm);
     wait_vmcnt<0>();
     __syncthreads();
@@ -672,38 +695,43 @@ __device__ __forceinline__ void attn_unit(const AttnParams &p, const int n, cons
     __syncthreads();
     if (!slast) return;
     if (active) {
-        // every split wrote (m, l, average) (m = -inf, l = 0, average = 0
-        // when empty): all S <= kTokenMaxSplits of them are requested before
-        // the first is used (one memory round trip, not one per split), then
-        // weighted and summed in split order
+        // every split wrote (m, l, acc) (m = -inf, l = 0, acc = 0 when empty):
+        // all S <= kTokenMaxSplits of them are requested at once (one memory
+        // round trip, not one per few splits), then weighted and summed in
+        // split order
+        static_assert(kTokenMaxSplits % 4 == 0, "partials named four at a time");
         const int S = p.splits;
-        uint64_t av[kTokenMaxSplits];
         f32x2 ml[kTokenMaxSplits];
+        u32x3 aw[kTokenMaxSplits];
 #pragma unroll
         for (int u = 0; u < kTokenMaxSplits; ++u) {
             if (u < S) {
-                av[u] = __hip_atomic_load((const uint64_t *)p.part_acc + part_acc_index(u, n, h, d0, N, p.Hq, D) / 4,
-                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                aw[u] = ld_coherent12_nowait((const uint32_t *)p.part_acc +
+                                             part_acc_index(u, n, h, d0, N, p.Hq, D) / 4 * 3);
                 ml[u] = ld_coherent2(p.part_ml + part_ml_index(u, n, h, N, p.Hq));
             } else {
-                av[u] = 0;
+                aw[u] = u32x3{0u, 0u, 0u};
                 ml[u] = f32x2{-INFINITY, 0.f};
             }
         }
+        // one wait for all of them; the empty statements after it (kept in
+        // order) name the loaded registers, so that no use of them is
+        // scheduled before the wait
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int u = 0; u < kTokenMaxSplits; u += 4)
+            asm volatile("" : "+v"(aw[u]), "+v"(aw[u + 1]), "+v"(aw[u + 2]), "+v"(aw[u + 3])::"memory");
         float m2 = -INFINITY, l2 = 0.f;
         f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < kTokenMaxSplits; ++u) {
             if (u < S) {
-                typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                const h2 lo = __builtin_bit_cast(h2, (uint32_t)av[u]), hi = __builtin_bit_cast(h2, (uint32_t)(av[u] >> 32));
-                const f32x4 avg = {(float)lo[0], (float)lo[1], (float)hi[0], (float)hi[1]};
                 const float mu = ml[u].x;
                 const float mn = fmaxf(m2, mu);
                 const float wo = (m2 == -INFINITY) ? 0.f : exp2_fast(m2 - mn);
                 const float wn = (mu == -INFINITY) ? 0.f : exp2_fast(mu - mn);
                 l2 = l2 * wo + ml[u].y * wn;
-                a2 = a2 * wo + avg * (ml[u].y * wn);
+                a2 = a2 * wo + unpack_f24x4(aw[u]) * wn;
                 m2 = mn;
             }
         }

@@ -116,9 +116,9 @@ hipError_t launch_prefill_select(const PrefillSelParams &p, int Di, hipStream_t 
 // contiguous:
 //   (m, l)       at part_ml[part_ml_index(s, n, h)]     (2 floats)
 //   acc[d]       at part_acc[part_acc_index(s, n, h, d)]
-// (the per-token MFMA unit, which merges its splits itself, leaves acc / l
-// instead, as fp16 at the same element positions of a half-size array:
-// ((_Float16 *)part_acc)[part_acc_index(s, n, h, d)])
+// (the per-token MFMA unit, which merges its splits itself, leaves acc as
+// 24-bit floats, four of them (index i .. i+3, i a multiple of 4) packed in
+// the three words at ((uint32_t *)part_acc)[i / 4 * 3])
 __host__ __device__ __forceinline__ int64_t part_ml_index(int s, int64_t n, int h, int64_t N, int Hq) {
     return (((int64_t)s * N + n) * Hq + h) * 2;
 }
