@@ -132,10 +132,17 @@ __device__ __forceinline__ int kswz(int key) {
     return ((key * CPR) >> 4) & (CPR - 1);
 }
 
-// V rows in LDS: 16-byte unit c of key k stored at unit c ^ vswz(k).  vswz
-// separates the 8 keys one ds_read_b64_tr_b8 group touches (keys 4a..4a+3 and
-// 16+4a..16+4a+3 of a 32-key chunk) onto distinct unit positions.
-__device__ __forceinline__ int vswz(int key) { return (key & 3) | (((key >> 4) & 1) << 2); }
+// V rows in LDS: 16-byte unit c of key k stored at unit c ^ vswz(k).  A
+// ds_read_b64_tr_b8 of 64 lanes is served 32 lanes (256 bytes, the 64 banks) a
+// cycle: two 16-lane groups, which read the 16-byte units of keys 4a..4a+3,
+// 16+4a..16+4a+3 and 4a+4..4a+7, 20+4a..20+4a+3 of a 32-key chunk (a even).
+// With 128-byte rows, key bit 0 already separates rows by half the banks;
+// vswz spreads the keys of each parity by their bits 1, 2 and 4 over the 8
+// unit positions, so that the 16 keys hit 16 distinct bank groups (keyed by
+// bits 0 and 1 and bit 4 alone, the two groups collided pairwise: rocprofv3
+// counted 64 bank-conflict cycles per wave of the attention launch, 32 with
+// this form, at the same launch time).
+__device__ __forceinline__ int vswz(int key) { return ((key >> 1) & 3) | (((key >> 4) & 1) << 2); }
 
 // PV k-order inside a 32-key chunk: MFMA k index 8*grp + e holds key
 //   e < 4 : 4*grp + e            (QK accumulator tile 0, row 4*grp + e)
