@@ -103,7 +103,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
     static_assert(MPC < 64, "page ids live one per lane");
     static_assert(NB == 2 || NB == 4, "one or two pages per group");
     static_assert(NLD <= NT && NLD % 64 == 0 && TPK * 16 * VPT == DI, "page slicing");
-    static_assert(NW * 16 * RB <= G * kBlock * RB, "query transpose area inside the first group");
+    static_assert(NW * 16 * RB <= G * kBlock * RB, "query transpose area inside the second group");
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -188,13 +188,28 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
         }
     }
 
+    // The first group to LDS as soon as its slices have landed, while the
+    // query rows are still on their way (they were requested after it); the
+    // next group's slices follow.  The second group's buffers stay free until
+    // the first group has been multiplied, so the query transpose below uses
+    // them and the first group's decode does not wait for it.
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+        if (cur[u] >= 0) store_page(pv[u], lds.kb[u]);
+    int nxt[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        nxt[u] = next_live();
+        if (nxt[u] >= 0) load_page(nxt[u], pv[u]);
+    }
+
     // B operand of S^T = K Q^T: for tile qt and k-step ks the lane holds
     // column 16*QT*wave + 16*qt + lane%16 at d = 32*ks + 8*(lane/16) .. +7.
-    // Each wave transposes through 16 rows of LDS of its own (inside the page
-    // buffers, before any page is stored there), 16-byte units XOR-swizzled
-    // by row so that neither side has bank conflicts.  LDS accesses of one
-    // wave complete in order, so the wave needs no barrier of its own.
-    uint8_t *const stage = &lds.kb[0][0] + wave * (16 * RB);
+    // Each wave transposes through 16 rows of LDS of its own (inside the
+    // second group's page buffers), 16-byte units XOR-swizzled by row so that
+    // neither side has bank conflicts.  LDS accesses of one wave complete in
+    // order, so the wave needs no barrier of its own.
+    uint8_t *const stage = &lds.kb[G][0] + wave * (16 * RB);
     uint4 qf[QT][KS];
     int vt[QT];
 #pragma unroll
@@ -227,18 +242,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillPages &pg, QRow qrow, 
         vmaxw = __builtin_amdgcn_readfirstlane((int)group_max<16>((float)mx));
     }
 
-    // first group to LDS (once every wave is done with its transpose area);
-    // the next group's slices on their way
-    __syncthreads();
-    int nxt[G];
-#pragma unroll
-    for (int u = 0; u < G; ++u)
-        if (cur[u] >= 0) store_page(pv[u], lds.kb[u]);
-#pragma unroll
-    for (int u = 0; u < G; ++u) {
-        nxt[u] = next_live();
-        if (nxt[u] >= 0) load_page(nxt[u], pv[u]);
-    }
+    // the first group is in LDS and every wave's transpose is done (the
+    // loop's first stores go to the transpose area)
     __syncthreads();
 
     const float scale = pg.scale;
