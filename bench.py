@@ -64,7 +64,7 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run a plain fp32 streaming kernel (out = in * 1) over this many MiB, "
                          "8 times, as the reference for HBM byte counters")
-    ap.add_argument("--calib-out", default=os.path.join(ROOT, "gpurun_out"),
+    ap.add_argument("--calib-out", default=".",
                     help="directory for calib.json (the copy size and the calls' algorithmic bytes)")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the dense bf16 K/V attention variant")
@@ -666,7 +666,7 @@ def hbm_calibration(torch, step_bytes: int, reps: int = 20) -> dict:
 def host_cores() -> tuple[int, int, int]:
     """(threads the oracle runs on, cores in this process's affinity mask, the
     host's hardware concurrency).  Worker pools stay within 16 threads, the CPU
-    share that comes with one GPU on the GPU machine, whatever the host has."""
+    share of one GPU of an 8-GPU host, whatever the host has."""
     try:
         aff = len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
