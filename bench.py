@@ -178,7 +178,7 @@ def ktrace_summary(run_dir: str, name: str, command: str) -> None:
     rows = list(csv.DictReader(open(files[0])))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = [f"# Kernel durations: {name}", "",
-             "Command (run from the repository root on the MI355X box):", "", f"    {command}", "",
+             "Command (run from the repository root on an MI355X host):", "", f"    {command}", "",
              f"rocprofv3 --kernel-trace --stats, all dispatches of the run; kernel sources digest "
              f"`{kernel_source_digest()}`.", "",
              "| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]

@@ -43,7 +43,7 @@ def test_algorithmic_bytes_by_hand():
 
 def test_copies_time_the_requested_steps():
     import bench
-    # the driver's request: 20 timed steps after 5 warmup steps, run exactly
+    # 20 timed steps after 5 warmup steps are run exactly
     assert bench.plan_copies(20, 5) == (5, 20, 5)
     assert bench.plan_copies(400, 40) == (8, 400, 40)
     for steps, warm in [(20, 5), (24, 6), (7, 0), (2000, 200), (17, 3), (1, 1)]:
