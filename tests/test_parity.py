@@ -266,6 +266,60 @@ def test_tokens_that_see_few_keys(msa, kv):
         f"oracle {ref[worst]!r} (visible keys {c.visible(worst[0])})")
 
 
+@pytest.mark.parametrize("kv", ["fp8", "bf16"])
+def test_splits_that_cancel(msa, kv):
+    """Split partials that cancel.  Every K code is 0, so every logit is 0 and
+    a token's output is the plain mean of the V rows of its 16 pages; the
+    first 8 pages hold non-negative codes and page 8 + j the rows of page
+    (j + 1) % 8 with the sign bit set (keys reversed), so the exact output is
+    0 while each split's accumulator (the sum of its two pages' V rows) is
+    large.  8 rows of one token each give every token 8 splits of 2 pages, and
+    no split holds the negation of another: the partials pass through the
+    workspace in their stored form and cancel in the merge, leaving only that
+    form's rounding.  Through
+    the per-token kernel and the one that selects in-launch, every output must
+    be within 2^-14 of 0 (a stored form with an 11-bit mantissa leaves about
+    1e-4 here, one with 16 bits about 1e-5)."""
+    import dataclasses
+    from msa_harness import poisoned, workspace
+    c = synth.small_fp8(R=8, T=1, lens=(16 * 128,) * 8, k=16, seed=6701)
+    assert c.MB == 16
+    bt = c.block_table.numpy()
+    kc, vc = c.k_cache.clone(), c.v_cache.clone()
+    kc[torch.from_numpy(bt.reshape(-1).astype(np.int64))] = 0
+    for r in range(c.R):
+        for j in range(8):
+            vc[int(bt[r, j])] &= 0x7F
+        for j in range(8):
+            vc[int(bt[r, j + 8])] = vc[int(bt[r, (j + 1) % 8])].flip(0) | 0x80
+    c = dataclasses.replace(c, k_cache=kc, v_cache=vc)
+    _say(f"case cancelling splits, kv {kv}: R={c.R} T={c.T} MB={c.MB} k={c.k}")
+    tk = torch.arange(c.k, dtype=torch.int32).repeat(c.N, 1)
+    ref = oracle_attention(c, tk.numpy())
+    assert np.abs(ref).max() == 0.0, "the construction leaves a nonzero exact output"
+    d = upload(c)
+    kd, vd = d.k_cache, d.v_cache
+    if kv == "bf16":
+        kd, vd = kd.to(torch.bfloat16), vd.to(torch.bfloat16)
+    ws = workspace(msa, c, c.k)
+    out = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_sparse_decode(d.q, kd, vd, d.block_table, d.seq_lens, tk.cuda(), c.T, out, c.sm_scale,
+                          c.k_scale, c.v_scale, c.B, ws)
+    sheet = torch.from_numpy(np.random.default_rng(6702).standard_normal((c.N, c.MB)).astype(np.float32))
+    t = poisoned((c.N, c.k), torch.int32)
+    out2 = poisoned((c.N, c.Hq, c.D), torch.bfloat16)
+    msa.msa_select_sparse_decode(sheet.cuda(), c.k, t, d.q, kd, vd, d.block_table, d.seq_lens, c.T,
+                                 out2, c.sm_scale, c.k_scale, c.v_scale, c.B, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(t.cpu(), tk), "with k = MB every block is selected, ascending"
+    for name, o in (("sparse_decode", out), ("select_sparse_decode", out2)):
+        check_attention(o, ref)
+        g = o.float().cpu().double().numpy()
+        worst = float(np.abs(g).max())
+        _say(f"{name}: largest |out| {worst:.3g}")
+        assert worst <= 2.0 ** -14, f"{name}: cancelling splits leave {worst:.3g}"
+
+
 def test_caller_topk_long_selection_with_gaps(msa):
     """Selections of more than 256 entries over more than 128 blocks (the
     token kernel resolves them from tables in LDS): -1 holes, ids >= MB,
